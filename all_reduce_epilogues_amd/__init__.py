@@ -1,1 +1,251 @@
-"""MI355X-native fused all-reduce epilogues (placeholder until the binding lands)."""
+"""MI355X (gfx950) fused all-reduce epilogues -- Python binding of libarepi.so.
+
+Thin ctypes layer over the C ABI declared in ``include/arepi.h``: it checks
+torch dtype, shape, device and contiguity, takes raw pointers and forwards them
+with the caller's (or the current) HIP stream.  Every step of the hot path runs
+in the library's HIP kernels; there is no fallback of any kind, and every call
+raises if ``libarepi.so`` is missing or a kernel launch is refused.
+
+Names mirror the C entry points without the ``arepi_`` prefix:
+  gemm_rs_fused, gemm_rs_supports, gemm_rs_flag_words, gemm_rs_pick_tile,
+  lamport_prefill, lamport_publish, ar_rmsnorm_lamport, combine_reduce,
+  emu_peer_producer, last_error, version.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libarepi.so")
+
+OK, EINVAL, EUNSUPPORTED, ELAUNCH = 0, -1, -2, -3
+SCOPE_AGENT, SCOPE_SYSTEM = 0, 1
+STATUS_TIMEOUT = 1
+TILE_AUTO, TILE_256x256, TILE_128x256, TILE_128x128, TILE_64x128, TILE_32x256 = range(6)
+TILE_NAMES = {TILE_256x256: "256x256", TILE_128x256: "128x256", TILE_128x128: "128x128",
+              TILE_64x128: "64x128", TILE_32x256: "32x256"}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class ArepiError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s (status %d)" % (msg, code))
+        self.code = code
+
+
+def lib():
+    """Load libarepi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libarepi.so is not built (expected at %s); run "
+                               "`python -m all_reduce_epilogues_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, u32p, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float
+        sig = {
+            "arepi_last_error": ([], ctypes.c_char_p),
+            "arepi_version": ([], ctypes.c_char_p),
+            "arepi_gemm_rs_supports": ([i64, i64, i64, i32, i32, i32, i32, i32, i32], i32),
+            "arepi_gemm_rs_flag_words": ([i64, i64, i32, i32, i32], i64),
+            "arepi_gemm_rs_pick_tile": ([i64, i64, i64, i32, i32, i32, i32, i32], i32),
+            "arepi_gemm_rs_fused": ([vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                     u32p, i64, vp], i32),
+            "arepi_lamport_prefill": ([vp, i64, vp], i32),
+            "arepi_lamport_publish": ([vp, vp, vp, i32, i64, i64, i32, i32, i32, vp], i32),
+            "arepi_ar_rmsnorm_lamport": ([vp, vp, vp, i64, i64, i32, f32, i32, u32p, i64, vp], i32),
+            "arepi_combine_reduce": ([vp, vp, vp, i64, i32, i64, vp], i32),
+            "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp], i32),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().arepi_last_error().decode()
+
+
+def version() -> str:
+    return lib().arepi_version().decode()
+
+
+def _check(rc: int, what: str) -> int:
+    if rc < 0:
+        raise ArepiError(rc, "%s: %s" % (what, last_error()))
+    return rc
+
+
+# ---- tensor checks (before any pointer is taken) -------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need(t, name, dtypes, shape=None, device=True):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s must have dtype %s, got %s" % (name, " or ".join(map(str, dtypes)), t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if device and t.device.type != "cuda":
+        raise ValueError("%s must live on the GPU, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _bf16(t, name, shape=None):
+    _need(t, name, (_torch().bfloat16,), shape)
+
+
+def _flags(t, name, shape=None):
+    torch = _torch()
+    _need(t, name, (torch.int32, torch.uint32), shape)
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---- GEMM + reduce-scatter --------------------------------------------------------
+
+def gemm_rs_flag_words(M: int, N: int, R: int, flag_tile_m: int = 128, flag_tile_n: int = 128) -> int:
+    return _check(lib().arepi_gemm_rs_flag_words(M, N, R, flag_tile_m, flag_tile_n), "gemm_rs_flag_words")
+
+
+def gemm_rs_supports(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publish=False, tile=TILE_AUTO) -> int:
+    """0 when supported, else the negative status (message in last_error())."""
+    return lib().arepi_gemm_rs_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish), tile)
+
+
+def gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publish=False) -> int:
+    return _check(lib().arepi_gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish)),
+                  "gemm_rs_pick_tile")
+
+
+def gemm_rs_fused(x, w, recv, ready_in, out, R: int, owner: int, send=None, ready_out=None,
+                  flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT,
+                  tile: int = TILE_AUTO, status=None, spin_limit: int = 0, stream=None):
+    """out[M/R,N] = bf16(X.W owner rows + sum of peers' recv); see include/arepi.h."""
+    _bf16(x, "x")
+    M, K = x.shape
+    _bf16(w, "w")
+    if w.shape[0] != K:
+        raise ValueError("w must be [K=%d, N], got %s" % (K, tuple(w.shape)))
+    N = w.shape[1]
+    if M % R:
+        raise ValueError("M=%d is not a multiple of R=%d" % (M, R))
+    seg = M // R
+    _bf16(out, "out", (seg, N))
+    if send is not None:
+        _bf16(send, "send", (M, N))
+    words = gemm_rs_flag_words(M, N, R, flag_tile_m, flag_tile_n)
+    if ready_in is not None:
+        _flags(ready_in, "ready_in", (R, words))
+    if ready_out is not None:
+        _flags(ready_out, "ready_out", (R, words))
+    if status is not None:
+        _flags(status, "status", (1,))
+    ptrs = (ctypes.c_void_p * R)()
+    if len(recv) != R:
+        raise ValueError("recv must list R=%d buffers (entry owner may be None)" % R)
+    for p in range(R):
+        if p == owner or recv[p] is None:
+            ptrs[p] = None
+            continue
+        _bf16(recv[p], "recv[%d]" % p, (seg, N))
+        ptrs[p] = recv[p].data_ptr()
+    rc = lib().arepi_gemm_rs_fused(_ptr(x), _ptr(w), ctypes.cast(ptrs, ctypes.c_void_p), _ptr(ready_in),
+                                   _ptr(out), _ptr(send), _ptr(ready_out), M, N, K, R, owner,
+                                   flag_tile_m, flag_tile_n, scope, tile, _ptr(status), spin_limit,
+                                   _stream(stream))
+    _check(rc, "gemm_rs_fused")
+
+
+def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N: int,
+                      flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT, stream=None):
+    """Test-only: land (peer, tile) items of src[p] into recv[p] and set their bits."""
+    seg = M // R
+    torch = _torch()
+    _need(order, "order", (torch.int32,))
+    if order.dim() != 2 or order.shape[1] != 2:
+        raise ValueError("order must be int32 [n_items, 2]")
+    words = gemm_rs_flag_words(M, N, R, flag_tile_m, flag_tile_n)
+    _flags(ready_in, "ready_in", (R, words))
+    sp = (ctypes.c_void_p * R)()
+    rp = (ctypes.c_void_p * R)()
+    for p in range(R):
+        if p == owner:
+            continue
+        _bf16(src[p], "src[%d]" % p, (seg, N))
+        _bf16(recv[p], "recv[%d]" % p, (seg, N))
+        sp[p] = src[p].data_ptr()
+        rp[p] = recv[p].data_ptr()
+    rc = lib().arepi_emu_peer_producer(ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p),
+                                       _ptr(ready_in), _ptr(order), order.shape[0], M, N, R, owner,
+                                       flag_tile_m, flag_tile_n, scope, _stream(stream))
+    _check(rc, "emu_peer_producer")
+
+
+# ---- Lamport AR + RMSNorm ------------------------------------------------------------
+
+def lamport_prefill(staging, stream=None):
+    _bf16(staging, "staging")
+    _check(lib().arepi_lamport_prefill(_ptr(staging), staging.numel(), _stream(stream)), "lamport_prefill")
+
+
+def lamport_publish(src, staging, order, tile_m: int = 128, tile_n: int = 128, scope: int = SCOPE_AGENT,
+                    stream=None):
+    """Emulated producers: src [S,M,N] -> staging [S,M,N] in order[s] tile order."""
+    _bf16(src, "src")
+    S, M, N = src.shape
+    _bf16(staging, "staging", (S, M, N))
+    torch = _torch()
+    tiles = -(-M // tile_m) * -(-N // tile_n)
+    _need(order, "order", (torch.int32,), (S, tiles))
+    _check(lib().arepi_lamport_publish(_ptr(src), _ptr(staging), _ptr(order), S, M, N, tile_m, tile_n, scope,
+                                       _stream(stream)), "lamport_publish")
+
+
+def ar_rmsnorm_lamport(staging, gamma, out, eps: float = 1e-6, scope: int = SCOPE_AGENT, status=None,
+                       spin_limit: int = 0, stream=None):
+    _bf16(staging, "staging")
+    S, M, N = staging.shape
+    _bf16(gamma, "gamma", (N,))
+    _bf16(out, "out", (M, N))
+    if status is not None:
+        _flags(status, "status", (1,))
+    _check(lib().arepi_ar_rmsnorm_lamport(_ptr(staging), _ptr(gamma), _ptr(out), M, N, S, float(eps), scope,
+                                          _ptr(status), spin_limit, _stream(stream)), "ar_rmsnorm_lamport")
+
+
+# ---- combine --------------------------------------------------------------------------
+
+def combine_reduce(x, gate, out, stream=None):
+    _bf16(x, "x")
+    T, E, H = x.shape
+    torch = _torch()
+    _need(gate, "gate", (torch.float32,), (T, E))
+    _bf16(out, "out", (T, H))
+    _check(lib().arepi_combine_reduce(_ptr(x), _ptr(gate), _ptr(out), T, E, H, _stream(stream)),
+           "combine_reduce")

@@ -1,0 +1,97 @@
+// emu_producer.hip -- stands in for the R-1 peer ranks on one GPU (tests and
+// benchmark only).  Each workgroup lands one (peer, flag tile) item: it copies
+// that tile of the peer's partial into recv[peer], drains its stores, meets the
+// workgroup barrier, and one thread publishes the tile's bit with a release --
+// the per-tile readiness of DeepGEMM PR #1 "Fused ring RS: per-tile bitmask",
+// in the place of a per-segment flag.
+#include <string>
+
+#include "arepi_internal.h"
+
+namespace arepi {
+namespace {
+
+constexpr int kMaxR = 8;
+
+struct EmuParams {
+    const uint16_t *src[kMaxR];
+    uint16_t *recv[kMaxR];
+    uint32_t *ready_in;
+    const int32_t *order;  // [n_items][2] = (peer, tile)
+    int64_t seg, N, ftiles_n, ftiles, fwords;
+    int ftm, ftn, R, owner, system_scope;
+};
+
+__global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
+    const int peer = p.order[2 * (int64_t)blockIdx.x];
+    const int64_t t = p.order[2 * (int64_t)blockIdx.x + 1];
+    const bool valid = peer >= 0 && peer < p.R && peer != p.owner && t >= 0 && t < p.ftiles;
+    if (!valid) return;  // uniform across the workgroup
+    const int64_t r0 = (t / p.ftiles_n) * p.ftm, c0 = (t % p.ftiles_n) * p.ftn;
+    const int64_t rows = min((int64_t)p.ftm, p.seg - r0);
+    const int64_t packs = min((int64_t)p.ftn, p.N - c0) / 8;
+    const uint16_t *s = nullptr;
+    uint16_t *d = nullptr;
+#pragma unroll
+    for (int i = 0; i < kMaxR; ++i)
+        if (i == peer) {
+            s = p.src[i];
+            d = p.recv[i];
+        }
+    for (int64_t i = threadIdx.x; i < rows * packs; i += blockDim.x) {
+        const int64_t off = (r0 + i / packs) * p.N + c0 + (i % packs) * 8;
+        *reinterpret_cast<uint4 *>(d + off) = *reinterpret_cast<const uint4 *>(s + off);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const bool sys = p.system_scope != 0;
+        fence_release(sys);
+        fetch_or_relaxed(p.ready_in + (int64_t)peer * p.fwords + (t >> 5), 1u << (t & 31), sys);
+    }
+}
+
+}  // namespace
+}  // namespace arepi
+
+using namespace arepi;
+
+extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
+                                       const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
+                                       int owner, int flag_tile_m, int flag_tile_n, int scope,
+                                       arepi_stream_t stream) {
+    auto bad = [](const std::string &m) { return fail(AREPI_EINVAL, "arepi_emu_peer_producer: " + m); };
+    if (R < 1 || R > kMaxR) return bad("R=" + std::to_string(R) + " outside [1, 8]");
+    if (owner < 0 || owner >= R) return bad("owner outside [0, R-1]");
+    if (M < 1 || M % R) return bad("M must be a positive multiple of R");
+    if (N < 8 || N % 8) return bad("N must be a positive multiple of 8");
+    if (flag_tile_m < 1 || flag_tile_n < 8 || flag_tile_n % 8)
+        return bad("flag tile needs flag_tile_m >= 1 and flag_tile_n a positive multiple of 8");
+    if (scope != AREPI_SCOPE_AGENT && scope != AREPI_SCOPE_SYSTEM) return bad("scope must be AGENT or SYSTEM");
+    if (n_items < 0 || n_items > (int64_t)1 << 30) return bad("n_items out of range");
+    if (n_items == 0) return ok();
+    if (!src || !recv || !ready_in || !order) return bad("src, recv, ready_in and order must be non-NULL");
+    EmuParams p{};
+    for (int i = 0; i < R; ++i) {
+        if (i == owner) continue;
+        if (!src[i] || !recv[i]) return bad("src/recv entry " + std::to_string(i) + " is NULL");
+        if (!aligned16(src[i]) || !aligned16(recv[i])) return bad("src/recv must be 16-byte aligned");
+        p.src[i] = src[i];
+        p.recv[i] = recv[i];
+    }
+    p.ready_in = ready_in;
+    p.order = order;
+    p.seg = M / R;
+    p.N = N;
+    p.ftiles_n = (N + flag_tile_n - 1) / flag_tile_n;
+    p.ftiles = ((p.seg + flag_tile_m - 1) / flag_tile_m) * p.ftiles_n;
+    p.fwords = (p.ftiles + 31) / 32;
+    p.ftm = flag_tile_m;
+    p.ftn = flag_tile_n;
+    p.R = R;
+    p.owner = owner;
+    p.system_scope = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
+    hipLaunchKernelGGL(emu_producer_kernel, dim3((unsigned)n_items), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), p);
+    return check_launch("arepi_emu_peer_producer");
+}

@@ -1,0 +1,276 @@
+"""Benchmark of the fused all-reduce epilogue hot path on one MI355X.
+
+Prints ONE JSON line.  Headline (`value`): GEMM + reduce-scatter epilogue on
+the tp=4 share -- X [4096,2048] . W [2048,4096] bf16, R=4, owner segment of 1024
+rows, three peer partials landed per 128x128 flag tile by an emulated-peer
+producer on a second stream in shuffled order -- as TFLOP/s of the whole step
+(2*M*N*K per step).  Inputs are resident in HBM before timing starts.
+
+Also reported in the same run: the Lamport AR+RMSNorm consumer (8 x
+[4096,7168]) and the weighted top-8 combine ([4096,8,7168]) as GB/s of
+algorithmic bytes, each against the 8 TB/s HBM peak; with --sweep the tp=8
+sweep (M = 256..8192, N=7168, K=2048) and the pre-staged tp=4 kernel.
+
+`cpu_baseline` times the CPU oracle (oracle/, test infrastructure) on a
+bounded row sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+LAMPORT_BYTES = 998_258_688 + 7168 * 2   # read 8P + write P + re-arm 8P (+ gamma)
+LAMPORT_BYTES_NO_REARM = 528_482_304 + 7168 * 2
+COMBINE_BYTES = 528_613_376              # read x + gate + write out
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sweep", action="store_true", help="also time the tp=8 sweep and the pre-staged tp=4 kernel")
+    ap.add_argument("--only", default=None, choices=[None, "gemm_rs", "lamport", "combine"],
+                    help="run a single path (used for per-kernel profiles)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return ap.parse_args()
+
+
+def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
+    """tp=4 share; producer stream lands the peers while the GEMM runs."""
+    dev = torch.device("cuda:0")
+    case = inputs.workload_gemm_rs(2)
+    M, N, K, R, owner = case["M"], case["N"], case["K"], case["R"], case["owner"]
+    seg = M // R
+
+    def up(a):
+        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+
+    x, w = up(case["x"]), up(case["w"])
+    src = [None if p == owner else up(case["recv"][p]) for p in range(R)]
+    recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
+    words = A.gemm_rs_flag_words(M, N, R)
+    tiles = ((seg + 127) // 128) * ((N + 127) // 128)
+    orders = [torch.from_numpy(inputs.producer_order(R, owner, tiles, 2000 + i)).to(dev) for i in range(4)]
+    rin = torch.zeros((R, words), dtype=torch.int32, device=dev)
+    rout = torch.zeros((R, words), dtype=torch.int32, device=dev)
+    out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
+    send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    tile = A.gemm_rs_pick_tile(M, N, K, R, owner, publish=True)
+    n_ev = steps + warmup
+    ev_gs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_ge = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_clear = [torch.cuda.Event() for _ in range(n_ev)]
+
+    def step(i):
+        # the previous step's GEMM must be done reading ready_in before it is cleared
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            rin.zero_()
+        ev_clear[i].record(side)
+        A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, owner, M, N, stream=side)
+        main.wait_event(ev_clear[i])
+        rout.zero_()
+        ev_gs[i].record(main)
+        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile,
+                        status=status, stream=main)
+        ev_ge[i].record(main)
+        main.wait_stream(side)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(warmup, warmup + steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    gemm_ms = sum(ev_gs[i].elapsed_time(ev_ge[i]) for i in range(warmup, warmup + steps)) / steps
+    if int(status.item()) != 0:
+        raise RuntimeError("a readiness wait timed out during the benchmark")
+    flops = 2.0 * M * N * K
+    return dict(ms_per_step=wall * 1e3, tflops=flops / wall / 1e12, gemm_ms=gemm_ms,
+                gemm_tflops=flops / (gemm_ms * 1e-3) / 1e12, tile=A.TILE_NAMES[tile], flops=flops,
+                M=M, N=N, K=K, R=R)
+
+
+def gemm_rs_prestaged(A, inputs, torch, steps, warmup, num, M=None):
+    dev = torch.device("cuda:0")
+    case = inputs.workload_gemm_rs(num, M=M)
+    M, N, K, R, owner = case["M"], case["N"], case["K"], case["R"], case["owner"]
+    seg = M // R
+
+    def up(a):
+        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+
+    x, w = up(case["x"]), up(case["w"])
+    recv = [None if p == owner else up(case["recv"][p]) for p in range(R)]
+    words = A.gemm_rs_flag_words(M, N, R)
+    tiles = ((seg + 127) // 128) * ((N + 127) // 128)
+    import numpy as np
+    full = np.zeros((R, words), np.uint32)
+    for p in range(R):
+        if p != owner:
+            for t in range(tiles):
+                full[p, t // 32] |= np.uint32(1 << (t % 32))
+    rin = torch.from_numpy(full.view(np.int32)).to(dev)
+    rout = torch.zeros((R, words), dtype=torch.int32, device=dev)
+    out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
+    send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    tile = A.gemm_rs_pick_tile(M, N, K, R, owner, publish=True)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(warmup):
+        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    flops = 2.0 * M * N * K
+    byts = 2.0 * (M * K + K * N + (R - 1) * seg * N + seg * N + (M - seg) * N)
+    return dict(M=M, N=N, K=K, R=R, tile=A.TILE_NAMES[tile], ms=ms, tflops=flops / ms / 1e9,
+                frac_mfma=flops / ms / 1e9 / PEAK_BF16_TFLOPS, gbs=byts / ms / 1e6,
+                frac_hbm=byts / ms / 1e6 / PEAK_HBM_GBS)
+
+
+def lamport(A, inputs, torch, steps, warmup):
+    dev = torch.device("cuda:0")
+    case = inputs.lamport_case()
+    S, M, N = case["S"], case["M"], case["N"]
+    src = torch.from_numpy(case["src"].view("int16")).view(torch.bfloat16).to(dev)
+    gamma = torch.from_numpy(case["gamma"].view("int16")).view(torch.bfloat16).to(dev)
+    order = torch.from_numpy(case["order"]).to(dev)
+    st = torch.empty((S, M, N), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    A.lamport_prefill(st)   # arming: once, before any timing
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    n = steps + warmup
+    es = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ee = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        side.wait_stream(main)   # publish only into re-armed staging
+        A.lamport_publish(src, st, order, stream=side)
+        main.wait_stream(side)
+        es[i].record(main)
+        A.ar_rmsnorm_lamport(st, gamma, out, case["eps"], status=status, stream=main)
+        ee[i].record(main)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("Lamport consumer timed out")
+    ms = sum(es[i].elapsed_time(ee[i]) for i in range(warmup, n)) / steps
+    return dict(ms=ms, gbs=LAMPORT_BYTES / ms / 1e6, frac_hbm=LAMPORT_BYTES / ms / 1e6 / PEAK_HBM_GBS,
+                gbs_no_rearm_bytes=LAMPORT_BYTES_NO_REARM / ms / 1e6, S=S, M=M, N=N)
+
+
+def combine(A, inputs, torch, steps, warmup):
+    dev = torch.device("cuda:0")
+    case = inputs.combine_case()
+    x = torch.from_numpy(case["x"].view("int16")).view(torch.bfloat16).to(dev)
+    gate = torch.from_numpy(case["gate"]).to(dev)
+    out = torch.empty((case["T"], case["H"]), dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        A.combine_reduce(x, gate, out)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        A.combine_reduce(x, gate, out)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    return dict(ms=ms, gbs=COMBINE_BYTES / ms / 1e6, frac_hbm=COMBINE_BYTES / ms / 1e6 / PEAK_HBM_GBS,
+                T=case["T"], E=case["E"], H=case["H"])
+
+
+def cpu_baseline(inputs):
+    """Oracle on a bounded row sample of the headline workload (~10 s)."""
+    import oracle
+    case = inputs.workload_gemm_rs(2)
+    M, N, K, R = case["M"], case["N"], case["K"], case["R"]
+    rows, t_used, r0, band = 0, 0.0, 0, 64
+    while t_used < 10.0 and r0 < M:
+        r1 = min(M, r0 + band)
+        t = time.perf_counter()
+        oracle.gemm_rs(case["x"], case["w"], case["recv"], R, case["owner"], rows=(r0, r1))
+        t_used += time.perf_counter() - t
+        rows += r1 - r0
+        r0 = r1
+        band = min(512, band * 2)
+    flops = 2.0 * rows * N * K
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "rows 0..%d of the tp=4 GEMM-RS workload (%d of %d rows, %.1f s of CPU time, %s)" % (
+                rows, rows, M, t_used, platform.processor() or platform.machine())}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only (this path has no multi-GPU run); got --gpus %d" % a.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import all_reduce_epilogues_amd as A
+    from all_reduce_epilogues_amd import inputs
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs the MI355X GPU")
+    A.lib()
+    secondary = {}
+    head = None
+    if a.only in (None, "gemm_rs"):
+        head = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup)
+    if a.only in (None, "lamport"):
+        secondary["lamport_ar_rmsnorm"] = lamport(A, inputs, torch, max(10, a.steps // 2), 3)
+    if a.only in (None, "combine"):
+        secondary["combine_reduce"] = combine(A, inputs, torch, max(10, a.steps // 2), 3)
+    if a.sweep:
+        secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2)
+        secondary["gemm_rs_tp8_sweep"] = [gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 3, M=m)
+                                         for m in inputs.TP8_M_SWEEP]
+    line = {
+        "metric": "GEMM-RS TFLOP/s + % bf16 MFMA peak; combine/RMSNorm GB/s + % HBM peak",
+        "value": head["tflops"] if head else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": head["ms_per_step"] if head else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gemm_rs tp4 share: X[4096,2048] x W[2048,4096] bf16, R=4, owner=0, "
+                               "3 peer partials [1024,4096] landed per 128x128 flag tile by a producer "
+                               "stream in shuffled order; send + ready_out published",
+                   "global_batch": 4096, "seq_len": None, "parallelism": "tp4 share on 1 GPU",
+                   "tile": head["tile"] if head else None},
+    }
+    if head:
+        achieved = head["flops"] / (head["gemm_ms"] * 1e-3) / 1e12
+        line["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                            "kernel": "gemm_rs_kernel", "avg_kernel_ms": head["gemm_ms"]}
+    line["secondary"] = secondary
+    if not a.no_cpu and head:
+        line["cpu_baseline"] = cpu_baseline(inputs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * arepi.h -- C ABI of the MI355X (gfx950) fused all-reduce epilogue library.
+ *
+ * Three operations of a tensor-parallel layer, each one hand-written HIP
+ * kernel, plus the calls that arm, feed and emulate the peers on one GPU:
+ *
+ *   arepi_gemm_rs_fused      row-parallel bf16 GEMM whose epilogue finishes the
+ *                            reduce-scatter of this rank's owner segment, gated
+ *                            per flag tile by a readiness bitmask.
+ *   arepi_ar_rmsnorm_lamport all-reduce combine + RMSNorm where the data is its
+ *                            own arrival flag (Lamport -0.0 sentinel).
+ *   arepi_combine_reduce     weighted top-k combine of expert outputs.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers into row-major, contiguous
+ *     buffers owned by the caller, 16-byte aligned.  Arrays of pointers marked
+ *     HOST are host arrays whose elements are device pointers.  bf16 data is
+ *     passed as uint16_t bit patterns.
+ *   - Every call validates all arguments before launching anything.  On bad
+ *     arguments it launches nothing, returns a negative arepi_status and records
+ *     a message naming the argument, the value given and the allowed range
+ *     (read it with arepi_last_error(), thread-local).
+ *   - Launches are asynchronous on `stream` (a hipStream_t; NULL is the legacy
+ *     default stream).  Device-side status words are read by the caller after
+ *     synchronising.  The library allocates no device memory and keeps no state
+ *     besides the per-thread error message.
+ *   - Spin waits are bounded: `spin_limit` is the number of polls before a wait
+ *     gives up (<= 0 selects about one second of polling); a wait that gives up
+ *     ORs AREPI_STATUS_TIMEOUT into *status (when status is non-NULL) and the
+ *     kernel finishes normally, with the affected outputs unspecified.
+ */
+#ifndef AREPI_H
+#define AREPI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *arepi_stream_t; /* same type as hipStream_t */
+
+typedef enum {
+    AREPI_OK = 0,
+    AREPI_EINVAL = -1,       /* null pointer, negative size, shape mismatch, misalignment */
+    AREPI_EUNSUPPORTED = -2, /* valid request outside what the kernels implement */
+    AREPI_ELAUNCH = -3       /* the HIP runtime refused the launch */
+} arepi_status;
+
+/* Memory scope of readiness flags: AGENT when producer and consumer share one
+ * GPU, SYSTEM when the producer is another device. */
+enum { AREPI_SCOPE_AGENT = 0, AREPI_SCOPE_SYSTEM = 1 };
+
+/* Bits ORed into a device status word. */
+enum { AREPI_STATUS_TIMEOUT = 1u };
+
+/* Compute-tile choice for arepi_gemm_rs_fused (0 = chosen from the shape). */
+enum {
+    AREPI_TILE_AUTO = 0,
+    AREPI_TILE_256x256 = 1,
+    AREPI_TILE_128x256 = 2,
+    AREPI_TILE_128x128 = 3,
+    AREPI_TILE_64x128 = 4,
+    AREPI_TILE_32x256 = 5
+};
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char *arepi_last_error(void);
+
+/* Library version string. */
+const char *arepi_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * GEMM + reduce-scatter epilogue.
+ *
+ * Defined by DeepGEMM PR #1 "Fused ring RS: per-tile bitmask + drain-ring with
+ * owner-boundary flush" (description: per-tile readiness replaces the
+ * per-segment flag; the epilogue adds the peers' partials of the owner
+ * segment) and ROCm/mori PR #662 (PR description: row-parallel wo_b GEMM fused
+ * with its all-reduce).  Here the combine is the direct sum over the R-1 peers.
+ *
+ * One rank of R computes its full local product C = X . W (fp32 accumulate):
+ *   x        bf16 [M,K]                X_r
+ *   w        bf16 [K,N]                W_r (row-major [K,N])
+ *   recv     HOST array of R device pointers; recv[p] is bf16 [M/R,N], peer p's
+ *            partial of this rank's owner segment; recv[owner] is ignored.
+ *   ready_in u32 [R][words]; bit t (word t/32, bit t%32) of peer p says flag
+ *            tile t of recv[p] has landed.  Read-only.  Flag tiles are
+ *            flag_tile_m x flag_tile_n pieces of a segment, clipped at its
+ *            edges, numbered row-major; words = arepi_gemm_rs_flag_words().
+ *   out      bf16 [M/R,N]: out[i,n] = bf16(C[owner*M/R + i, n] + sum over
+ *            p != owner of recv[p][i,n]) (fp32 adds, round-to-nearest-even).
+ *   send     bf16 [M,N] or NULL: rows outside the owner segment receive
+ *            bf16(C) -- this rank's outgoing partials; owner rows untouched.
+ *   ready_out u32 [R][words] or NULL (requires send): after the call every
+ *            flag tile of every non-owner segment has its bit set, each set
+ *            with a release at `scope` once that tile's send rows are stored.
+ *   status   device u32 or NULL; spin_limit as above.
+ * Owner tiles wait for their ready_in bits with an acquire at `scope`.
+ * Constraints: 1 <= R <= 8, 0 <= owner < R, M % R == 0, M >= 1, N >= 8,
+ * N % 8 == 0, K >= 8, K % 8 == 0, flag tiles >= 1x1.  With ready_out, flag
+ * tiles must nest inside the compute tiles (see arepi_gemm_rs_supports).
+ * ------------------------------------------------------------------------ */
+int arepi_gemm_rs_supports(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
+                           int flag_tile_n, int publish, int tile_cfg);
+
+/* u32 words per peer of ready_in / ready_out, or a negative status. */
+int64_t arepi_gemm_rs_flag_words(int64_t M, int64_t N, int R, int flag_tile_m, int flag_tile_n);
+
+/* Compute tile (AREPI_TILE_*) the automatic choice picks for a shape, or a
+ * negative status. */
+int arepi_gemm_rs_pick_tile(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
+                            int flag_tile_n, int publish);
+
+int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const uint16_t *const *recv,
+                        const uint32_t *ready_in, uint16_t *out, uint16_t *send,
+                        uint32_t *ready_out, int64_t M, int64_t N, int64_t K, int R, int owner,
+                        int flag_tile_m, int flag_tile_n, int scope, int tile_cfg,
+                        uint32_t *status, int64_t spin_limit, arepi_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Lamport all-reduce + RMSNorm.
+ *
+ * Defined by ROCm/aiter PR #4977 "[HIP] Single-kernel Lamport fused all-reduce
+ * + RMSNorm (opt-in)", Approach section: staging is armed with -0.0 (bf16
+ * 0x8000); producers map -0.0 to +0.0 before storing; a consumer treats a
+ * 16-byte pack as arrived only when none of its words is 0x8000, consumes it
+ * and re-arms it.  The staging area is private to these calls.
+ * ------------------------------------------------------------------------ */
+
+/* Arm: write 0x8000 into every one of `elems` bf16 words of staging.  Call once
+ * before first use, outside any graph capture (after that the consumer keeps
+ * the area armed). */
+int arepi_lamport_prefill(uint16_t *staging, int64_t elems, arepi_stream_t stream);
+
+/* Emulated producers for one GPU: for each slot s < S, copy src[s] (bf16
+ * [M,N]) into staging[s] one tile_m x tile_n tile at a time, in the order
+ * order[s][0..tiles-1] (device int32, a permutation of the row-major tile
+ * ids), canonicalising every 0x8000 word to 0x0000 and storing with
+ * device-coherent stores at `scope`.  No fence: the data is the flag.
+ * src and staging are [S][M][N]. */
+int arepi_lamport_publish(const uint16_t *src, uint16_t *staging, const int32_t *order, int S,
+                          int64_t M, int64_t N, int tile_m, int tile_n, int scope,
+                          arepi_stream_t stream);
+
+/* Consumer: staging [S][M][N] (armed, being or already published), gamma bf16
+ * [N], out bf16 [M,N].  Per row i: s = sum over slots 0..S-1 (fp32) once each
+ * pack has arrived; out = bf16(s * (1/sqrt(mean(s^2) + eps)) * gamma).  Every
+ * consumed pack is re-armed, so staging is all 0x8000 again on return.
+ * Constraints: 1 <= S <= 8, N % 8 == 0, 8 <= N <= 16384. */
+int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma, uint16_t *out, int64_t M,
+                             int64_t N, int S, float eps, int scope, uint32_t *status,
+                             int64_t spin_limit, arepi_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Weighted top-k combine.
+ *
+ * The expert-output reduction of DeepEP's intranode combine (DeepEP PR #527,
+ * "Fix the MultiStages for intranode combine": a multi-stage pipeline whose
+ * stages are issued and waited on independently):
+ *   out[t,h] = bf16( sum_{k<E} gate[t,k] * x[t,k,h] )    (fp32 accumulate)
+ *   x bf16 [T,E,H], gate fp32 [T,E], out bf16 [T,H].
+ * Constraints: 1 <= E <= 16, H % 8 == 0.
+ * ------------------------------------------------------------------------ */
+int arepi_combine_reduce(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int E,
+                         int64_t H, arepi_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * Test-only peer emulation on one GPU (prefixed emu_ so it is never mistaken
+ * for the method).  For each item j < n_items, order[j] = (peer p, flag tile
+ * t): copy flag tile t of src[p] (bf16 [M/R,N]) into recv[p], then set bit t
+ * of ready_in[p] with a release at `scope`.  src and recv are HOST arrays of R
+ * device pointers (entry `owner` ignored); ready_in must be zero beforehand.
+ * ------------------------------------------------------------------------ */
+int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
+                            const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
+                            int owner, int flag_tile_m, int flag_tile_n, int scope,
+                            arepi_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AREPI_H */

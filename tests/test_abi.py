@@ -1,0 +1,152 @@
+"""The C-ABI library loads, exports every symbol include/arepi.h declares, and
+rejects bad arguments before launching anything (CPU only: no call here
+reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import all_reduce_epilogues_amd as A
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "arepi.h")).read()
+    return sorted(set(re.findall(r"\b(arepi_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = A.lib()
+    names = declared_symbols()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+        assert getattr(lib, n) is not None
+
+
+def test_version_and_empty_error():
+    assert "gfx950" in A.version()
+
+
+@pytest.mark.parametrize("M,N,R,ftm,ftn", [
+    (256, 512, 2, 128, 128), (4096, 4096, 4, 128, 128), (256, 7168, 8, 128, 128),
+    (8192, 7168, 8, 128, 128), (200, 520, 2, 32, 64), (24, 8, 8, 1, 8), (1056, 64, 1, 32, 32),
+])
+def test_flag_words_agree_with_oracle(M, N, R, ftm, ftn):
+    assert A.gemm_rs_flag_words(M, N, R, ftm, ftn) == oracle.flag_words(M, N, R, ftm, ftn)
+
+
+def nests(M, N, R, ftm, ftn, BM, BN):
+    """Brute force: every flag tile lies inside one compute tile."""
+    seg = M // R
+    for c0 in range(0, N, ftn):
+        c1 = min(c0 + ftn, N) - 1
+        if c0 // BN != c1 // BN:
+            return False
+    for d in range(R):
+        for r0 in range(0, seg, ftm):
+            s, e = d * seg + r0, d * seg + min(r0 + ftm, seg) - 1
+            if s // BM != e // BM:
+                return False
+    return True
+
+
+TILE_DIMS = {A.TILE_256x256: (256, 256), A.TILE_128x256: (128, 256), A.TILE_128x128: (128, 128),
+             A.TILE_64x128: (64, 128), A.TILE_32x256: (32, 256)}
+
+
+@pytest.mark.parametrize("M,N,R,ftm,ftn", [
+    (256, 512, 2, 128, 128), (256, 7168, 8, 128, 128), (1024, 7168, 8, 128, 128),
+    (200, 520, 2, 32, 64), (96, 72, 4, 24, 8), (192, 256, 3, 64, 128), (512, 512, 2, 256, 256),
+])
+def test_supports_matches_flag_nesting(M, N, R, ftm, ftn):
+    for tile, (BM, BN) in TILE_DIMS.items():
+        rc = A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=True, tile=tile)
+        assert (rc == 0) == nests(M, N, R, ftm, ftn, BM, BN), (tile, A.last_error())
+        # without publication every tile is allowed
+        assert A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=False, tile=tile) == 0
+
+
+def test_auto_tile_is_supported():
+    for M in (256, 1024, 4096, 8192):
+        t = A.gemm_rs_pick_tile(M, 7168, 2048, 8, 0, 128, 128, publish=True)
+        assert A.gemm_rs_supports(M, 7168, 2048, 8, 0, 128, 128, publish=True, tile=t) == 0
+
+
+@pytest.mark.parametrize("args,needle", [
+    ((256, 512, 256, 0, 0), "R=0"),
+    ((256, 512, 256, 9, 0), "R=9"),
+    ((256, 512, 256, 2, 2), "owner=2"),
+    ((255, 512, 256, 2, 0), "not a multiple of R"),
+    ((256, 500, 256, 2, 0), "N=500"),
+    ((256, 512, 250, 2, 0), "K=250"),
+    ((0, 512, 256, 1, 0), "M=0"),
+])
+def test_gemm_rs_rejects_bad_shapes(args, needle):
+    M, N, K, R, owner = args
+    rc = A.gemm_rs_supports(M, N, K, R, owner, 128, 128)
+    assert rc == A.EINVAL
+    assert needle in A.last_error()
+
+
+def test_gemm_rs_fused_validates_before_launch():
+    L = A.lib()
+    vp = ctypes.c_void_p
+    # NULL x: rejected by name, nothing launched
+    rc = L.arepi_gemm_rs_fused(None, None, None, None, None, None, None, 256, 512, 256, 2, 0, 128, 128,
+                               0, 0, None, 0, None)
+    assert rc == A.EINVAL and "non-NULL" in A.last_error()
+    # bad scope value
+    buf = ctypes.create_string_buffer(64)
+    p = vp(ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16)
+    recv = (vp * 2)(None, p)
+    rc = L.arepi_gemm_rs_fused(p, p, ctypes.cast(recv, vp), p, p, None, None, 256, 512, 256, 2, 0, 128, 128,
+                               7, 0, None, 0, None)
+    assert rc == A.EINVAL and "scope=7" in A.last_error()
+    # ready_out without send
+    rc = L.arepi_gemm_rs_fused(p, p, ctypes.cast(recv, vp), p, p, None, p, 256, 512, 256, 2, 0, 128, 128,
+                               0, 0, None, 0, None)
+    assert rc == A.EINVAL and "ready_out needs send" in A.last_error()
+    # misaligned pointer
+    bad = vp(p.value + 2)
+    rc = L.arepi_gemm_rs_fused(bad, p, ctypes.cast(recv, vp), p, p, None, None, 256, 512, 256, 2, 0, 128, 128,
+                               0, 0, None, 0, None)
+    assert rc == A.EINVAL and "aligned" in A.last_error()
+    # unknown tile id
+    rc = L.arepi_gemm_rs_fused(p, p, ctypes.cast(recv, vp), p, p, None, None, 256, 512, 256, 2, 0, 128, 128,
+                               0, 42, None, 0, None)
+    assert rc == A.EINVAL and "tile_cfg=42" in A.last_error()
+    # flag tiles that straddle the forced compute tile, with publication
+    rc = L.arepi_gemm_rs_fused(p, p, ctypes.cast(recv, vp), p, p, p, p, 256, 512, 256, 2, 0, 128, 128,
+                               0, A.TILE_64x128, None, 0, None)
+    assert rc == A.EUNSUPPORTED and "straddle" in A.last_error()
+
+
+def test_lamport_and_combine_validate_before_launch():
+    L = A.lib()
+    assert L.arepi_ar_rmsnorm_lamport(None, None, None, 4, 64, 9, 1e-6, 0, None, 0, None) == A.EINVAL
+    assert "S=9" in A.last_error()
+    assert L.arepi_ar_rmsnorm_lamport(None, None, None, 4, 20000, 8, 1e-6, 0, None, 0, None) == A.EUNSUPPORTED
+    assert L.arepi_ar_rmsnorm_lamport(None, None, None, 4, 60, 8, 1e-6, 0, None, 0, None) == A.EINVAL
+    assert L.arepi_ar_rmsnorm_lamport(None, None, None, 4, 64, 8, 1e-6, 0, None, 0, None) == A.EINVAL
+    assert "non-NULL" in A.last_error()
+    assert L.arepi_ar_rmsnorm_lamport(None, None, None, 0, 64, 8, 1e-6, 0, None, 0, None) == A.OK  # empty
+    assert L.arepi_lamport_publish(None, None, None, 8, 4, 64, 128, 12, 0, None) == A.EINVAL
+    assert L.arepi_lamport_prefill(None, -1, None) == A.EINVAL
+    assert L.arepi_lamport_prefill(None, 0, None) == A.OK
+    assert L.arepi_combine_reduce(None, None, None, 4, 17, 64, None) == A.EUNSUPPORTED
+    assert "E=17" in A.last_error()
+    assert L.arepi_combine_reduce(None, None, None, 4, 8, 60, None) == A.EINVAL
+    assert L.arepi_combine_reduce(None, None, None, 0, 8, 64, None) == A.OK  # empty: nothing to do
+    assert L.arepi_combine_reduce(None, None, None, 4, 8, 64, None) == A.EINVAL
+    assert L.arepi_emu_peer_producer(None, None, None, None, 1, 256, 512, 2, 5, 128, 128, 0, None) == A.EINVAL
+
+
+def test_binding_checks_dtype_before_pointers():
+    import torch
+    x = torch.zeros(4, 8, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        A.combine_reduce(x, x, x)

@@ -1,0 +1,207 @@
+"""GPU parity of arepi_gemm_rs_fused against the CPU oracle.
+
+Inputs come from the seeded generators; expected values only from oracle/.
+bf16 outputs within |d| <= 1e-2|ref| + 1e-3; ready_out bit-exact; ready_in
+unchanged; owner rows of `send` untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import all_reduce_epilogues_amd as A
+import oracle
+from all_reduce_epilogues_amd import inputs
+from conftest import read_golden
+from gpu_util import (assert_bf16_close, device, flag_words_all_set, from_dev_bf16, from_dev_u32,
+                      to_dev_bf16, to_dev_u32)
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL_FILL = 0x7FC1  # a NaN pattern no correct output produces
+
+
+def run(case, tile=A.TILE_AUTO, publish=True, ftm=128, ftn=128, stream=None, status=None, spin_limit=0,
+        ready_in=None, want_send=True):
+    dev = device()
+    M, N, R, owner = case["M"], case["N"], case["R"], case["owner"]
+    seg = M // R
+    x = to_dev_bf16(case["x"])
+    w = to_dev_bf16(case["w"])
+    recv = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
+    tiles = oracle.flag_tiles(M, N, R, ftm, ftn)
+    rin_np = flag_words_all_set(R, owner, tiles) if ready_in is None else ready_in
+    rin = to_dev_u32(rin_np)
+    out = torch.full((seg, N), 0, dtype=torch.int16, device=dev).fill_(SENTINEL_FILL).view(torch.bfloat16)
+    send = None
+    if want_send:
+        send = torch.full((M, N), SENTINEL_FILL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    rout = torch.zeros(rin.shape, dtype=torch.int32, device=dev) if (publish and want_send) else None
+    A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, flag_tile_m=ftm,
+                    flag_tile_n=ftn, tile=tile, status=status, spin_limit=spin_limit, stream=stream)
+    torch.cuda.synchronize()
+    res = dict(out=from_dev_bf16(out), send=from_dev_bf16(send) if send is not None else None,
+               ready_out=from_dev_u32(rout) if rout is not None else None, ready_in=from_dev_u32(rin))
+    assert np.array_equal(res["ready_in"], rin_np), "ready_in must be read-only"
+    return res
+
+
+def check_against_oracle(case, res, ftm=128, ftn=128, rows=None, what=""):
+    M, N, R, owner = case["M"], case["N"], case["R"], case["owner"]
+    seg = M // R
+    if rows is None:
+        ref_out, ref_send = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
+        assert_bf16_close(res["out"], ref_out, what + " out")
+        if res["send"] is not None:
+            mask = np.ones(M, bool)
+            mask[owner * seg:(owner + 1) * seg] = False
+            assert_bf16_close(res["send"][mask], ref_send[mask], what + " send")
+            assert np.all(res["send"][~mask] == SENTINEL_FILL), what + " owner rows of send were written"
+    else:
+        for r0, r1 in rows:
+            ref_out, ref_send = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner, rows=(r0, r1))
+            for i in range(r0, r1):
+                if owner * seg <= i < (owner + 1) * seg:
+                    li = i - owner * seg
+                    assert_bf16_close(res["out"][li], ref_out[li], "%s out row %d" % (what, i))
+                elif res["send"] is not None:
+                    assert_bf16_close(res["send"][i], ref_send[i], "%s send row %d" % (what, i))
+    if res["ready_out"] is not None:
+        assert np.array_equal(res["ready_out"], oracle.ready_out(M, N, R, owner, ftm, ftn)), what + " ready_out"
+
+
+def tiles_to_try(case, ftm, ftn):
+    for t in (A.TILE_256x256, A.TILE_128x256, A.TILE_128x128, A.TILE_64x128, A.TILE_32x256):
+        pub = A.gemm_rs_supports(case["M"], case["N"], case["K"], case["R"], case["owner"], ftm, ftn,
+                                 publish=True, tile=t) == 0
+        yield t, pub
+
+
+@pytest.mark.parametrize("owner", [0, 1])
+def test_tiny_workload_every_tile(owner):
+    case = inputs.workload_gemm_rs(1, owner=owner)
+    for tile, pub in tiles_to_try(case, 128, 128):
+        print("tiny workload owner=%d tile=%s publish=%s" % (owner, A.TILE_NAMES[tile], pub), flush=True)
+        res = run(case, tile=tile, publish=pub)
+        check_against_oracle(case, res, what="tiny/%s" % A.TILE_NAMES[tile])
+
+
+@pytest.mark.parametrize("M,N,K,R,owner,ftm,ftn", [
+    (200, 520, 200, 2, 1, 32, 64),    # ragged M tile, N and K tails
+    (96, 72, 8, 4, 2, 24, 8),         # K smaller than one k-step
+    (24, 8, 16, 8, 7, 3, 8),          # one pack wide, 3-row segments
+    (192, 264, 136, 3, 1, 64, 8),     # R=3
+    (640, 384, 328, 1, 0, 128, 128),  # R=1: a plain GEMM
+    (520, 1032, 72, 8, 4, 128, 128),  # 65-row segments straddling every tile
+])
+def test_ragged_shapes_every_tile(M, N, K, R, owner, ftm, ftn):
+    case = inputs.gemm_rs_case(M, N, K, R, owner=owner, seed=7 + M + N + K)
+    for tile, pub in tiles_to_try(case, ftm, ftn):
+        print("ragged %s tile=%s publish=%s" % ((M, N, K, R, owner), A.TILE_NAMES[tile], pub), flush=True)
+        res = run(case, tile=tile, publish=pub, ftm=ftm, ftn=ftn)
+        check_against_oracle(case, res, ftm, ftn, what="ragged/%s" % A.TILE_NAMES[tile])
+
+
+def test_golden_all_ones_two_ranks_on_gpu():
+    g = read_golden("gemm_ar_all_ones.txt")
+    M, N, K, R = g["M"], g["N"], g["K"], g["ranks"]
+    ones = np.full((M, K), 0x3F80, np.uint16)
+    case = dict(M=M, N=N, K=K, R=R, owner=0, x=ones, w=np.full((K, N), 0x3F80, np.uint16),
+                recv=[None, np.full((M // R, N), 0x4400, np.uint16)])  # peer partial = 512
+    res = run(case)
+    assert np.all(res["out"] == g["expected_output_bf16"])
+
+
+def test_golden_rank_plus_one_on_gpu():
+    g = read_golden("self_test_rank_plus_one.txt")
+    for R, expect in zip(g["world_sizes"], g["expected"]):
+        owner = R - 1
+        K = 8 * (owner + 1)  # local partial = K/8 * 8 ones... = owner + 1 via w = 1/8
+        M, N = 16 * R, 64
+        x = np.full((M, K), 0x3F80, np.uint16)                 # 1.0
+        w = np.full((K, N), 0x3E00, np.uint16)                 # 0.125
+        recv = [None if p == owner else
+                np.full((M // R, N), np.float32(p + 1).view(np.uint32) >> 16, np.uint16) for p in range(R)]
+        res = run(dict(M=M, N=N, K=K, R=R, owner=owner, x=x, w=w, recv=recv))
+        vals = (res["out"].astype(np.uint32) << 16).view(np.float32)
+        assert np.all(vals == expect), (R, np.unique(vals))
+
+
+@pytest.mark.parametrize("R,owner", [(2, 0), (4, 3), (8, 5)])
+def test_exact_integer_linearity_on_gpu(R, owner):
+    rng = np.random.default_rng(500 + R)
+    M, N, Kr = 64 * R, 136, 16
+    Xf = rng.integers(-2, 3, size=(M, R * Kr))
+    Wf = rng.integers(-2, 3, size=(R * Kr, N))
+    seg = M // R
+
+    def bits(a):
+        return (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+    parts = [Xf[:, p * Kr:(p + 1) * Kr] @ Wf[p * Kr:(p + 1) * Kr] for p in range(R)]
+    case = dict(M=M, N=N, K=Kr, R=R, owner=owner, x=bits(Xf[:, owner * Kr:(owner + 1) * Kr]),
+                w=bits(Wf[owner * Kr:(owner + 1) * Kr]),
+                recv=[None if p == owner else bits(parts[p][owner * seg:(owner + 1) * seg]) for p in range(R)])
+    res = run(case)
+    assert np.array_equal(res["out"], bits((Xf @ Wf)[owner * seg:(owner + 1) * seg]))
+
+
+def test_tp4_workload_prestaged_and_concurrent_producer():
+    case = inputs.workload_gemm_rs(2)
+    M, N, R, owner = case["M"], case["N"], case["R"], case["owner"]
+    seg = M // R
+    pre = run(case)
+    # owner segment in full, send rows sampled from every segment
+    rows = [(0, seg)] + [(d * seg + o, d * seg + o + 16) for d in range(1, R) for o in (0, 509, seg - 16)]
+    check_against_oracle(case, pre, rows=rows, what="tp4 prestaged")
+    rerun = run(case)
+    assert np.array_equal(pre["out"], rerun["out"]) and np.array_equal(pre["send"], rerun["send"])
+
+    # concurrent: an emulated-peer producer on a second stream lands the peer
+    # partials in a shuffled tile order while the GEMM runs
+    dev = device()
+    tiles = oracle.flag_tiles(M, N, R, 128, 128)
+    for seed in (11, 12):
+        order = torch.from_numpy(inputs.producer_order(R, owner, tiles, seed)).to(dev)
+        src = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
+        recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
+        rin = torch.zeros((R, A.gemm_rs_flag_words(M, N, R)), dtype=torch.int32, device=dev)
+        out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
+        send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        rout = torch.zeros_like(rin)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        x, w = to_dev_bf16(case["x"]), to_dev_bf16(case["w"])
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        main = torch.cuda.current_stream()
+        A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, stream=side)
+        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, status=status, stream=main)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, "a readiness wait timed out"
+        assert np.array_equal(from_dev_bf16(out), pre["out"]), "result depends on arrival order"
+        assert np.array_equal(from_dev_u32(rin), flag_words_all_set(R, owner, tiles))
+
+
+@pytest.mark.parametrize("M,owner", [(256, 0), (1024, 0), (1024, 7), (4096, 0), (8192, 0)])
+def test_tp8_workload_sweep(M, owner):
+    case = inputs.workload_gemm_rs(3, M=M, owner=owner)
+    R = 8
+    seg = M // R
+    res = run(case)
+    rows = [(owner * seg, (owner + 1) * seg)]
+    rows += [(d * seg, d * seg + min(8, seg)) for d in range(R) if d != owner]
+    rows += [(d * seg + seg - min(8, seg), d * seg + seg) for d in range(R) if d != owner]
+    check_against_oracle(case, res, rows=rows, what="tp8 M=%d" % M)
+
+
+def test_timeout_reports_status_and_finishes():
+    case = inputs.workload_gemm_rs(1)
+    R, owner = case["R"], case["owner"]
+    tiles = oracle.flag_tiles(case["M"], case["N"], R, 128, 128)
+    rin = flag_words_all_set(R, owner, tiles)
+    rin[1, 0] &= ~np.uint32(1 << 2)  # one peer tile never lands
+    status = torch.zeros(1, dtype=torch.int32, device=device())
+    res = run(case, ready_in=rin, status=status, spin_limit=2000)
+    assert int(status.item()) & A.STATUS_TIMEOUT
+    # send rows do not depend on the missing tile
+    _, ref_send = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
+    assert_bf16_close(res["send"][128:], ref_send[128:], "send after timeout")
