@@ -49,7 +49,8 @@ constexpr int kXcds = 8;
 struct GemmRsParams {
     const uint16_t *x;
     const uint16_t *w;
-    const uint16_t *recv[kMaxR];
+    const uint16_t *peer[kMaxR - 1];  // peer partials in ascending rank order, owner skipped
+    int npeers;                       // R - 1
     const uint32_t *ready_in;
     uint16_t *out;
     uint16_t *send;
@@ -64,21 +65,45 @@ struct GemmRsParams {
     int nRB, nCB, ob1, group, xcd_chunk, nWG;
 };
 
-__device__ __forceinline__ uint32_t dword_of(const uint4 &v, int d) {
-    return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
-}
+// gfx9 buffer-resource word 3 (raw, untyped 32-bit data format).
+constexpr int kBufferDword3 = 0x00020000;
 
-// 16-byte load, or zeros when `pred` is false (returned by value so the
-// compiler never needs the address of a zero constant).
-__device__ __forceinline__ uint4 load16_or_zero(const uint16_t *p, bool pred) {
-    uint4 r = make_uint4(0u, 0u, 0u, 0u);
-    if (pred) r = *reinterpret_cast<const uint4 *>(p);
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// X tile rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r sits at
+// c ^ ((r >> 1) & 7): 16 consecutive rows reading one logical chunk hit 16
+// distinct 16-byte bank groups (row parity x 8 chunks).
+__device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
+// W tile rows are BN*2 bytes (BN/8 chunks); chunk c of row k sits at
+// c ^ (4 * (k & 3)): the four rows and four chunks one transpose read touches
+// per 16-lane group land in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
+
+// s_waitcnt vmcnt(0) with a memory clobber (the compiler neither drops it nor
+// moves memory operations across it).
+__device__ __forceinline__ void wait_vmcnt_zero() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void drain_stores() { wait_vmcnt_zero(); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (base, no stride, num_records bytes, gfx9 word 3).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    i32x4 r = {(int)(uint32_t)b, (int)(uint32_t)(b >> 32), (int)bytes, kBufferDword3};
     return r;
 }
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-// Offset (in bf16 elements) of 16-byte chunk c of row r of a [rows][BK] tile.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * BK + ((c ^ swz(r)) << 3); }
+// 16-byte direct-to-LDS load: lane i's 16 bytes from rsrc + voff + soff land
+// at LDS byte lds_base + 16*i.  Issued as asm so the compiler does not add
+// its own conservative waits between these loads and LDS reads; every stage
+// is drained explicitly (wait_vmcnt_zero + barrier) before it is read.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
 
 __device__ __forceinline__ void tile_of_block(const GemmRsParams &p, int b, int &rb, int &cb) {
     // XCD-aware remap inside full rounds of 8*C blocks: consecutive schedule
@@ -99,21 +124,29 @@ __device__ __forceinline__ void tile_of_block(const GemmRsParams &p, int b, int 
     rb = (p.ob1 + pos) % p.nRB;  // rotated: owner row blocks come last
 }
 
-template <int BM, int BN, int WM, int WN>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1)
+template <int BM, int BN, int WM, int WN, int PEERS>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
     gemm_rs_kernel(const GemmRsParams p) {
     constexpr int NWN = BN / WN;
-    constexpr int NT = (BM / WM) * NWN * 64;
+    constexpr int NW = (BM / WM) * NWN;
     constexpr int TM = WM / 32, TN = WN / 32;
-    constexpr int A_LD = BM * (BK / 8) / NT;        // 16-byte X chunks per thread
-    constexpr int B_LD = (BK / 4) * (BN / 8) / NT;  // 4x8 W blocks per thread
-    constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;
-    constexpr int EPS = WN + 8;                      // epilogue LDS row stride (floats)
-    static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for the thread count");
-    static_assert(A_LD * NT == BM * (BK / 8) && B_LD * NT == (BK / 4) * (BN / 8), "uneven load split");
-    static_assert((BM / WM) * NWN * 32 * EPS * 4 <= 2 * (A_ELEMS + B_ELEMS) * 2, "epilogue LDS");
+    constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;  // one stage
+    constexpr int A_INSTR = A_BYTES / 1024 / NW;  // 1 KiB direct-to-LDS loads per wave
+    constexpr int B_INSTR = B_BYTES / 1024 / NW;
+    constexpr int B_CPR = BN / 8;                 // 16-byte chunks per W row in LDS
+    constexpr int B_RPI = 64 / B_CPR;             // W rows per load instruction
+    constexpr int EPS = WN + 8;                   // epilogue LDS row stride (floats)
+    // epilogue slab rows: the largest of 32/16/8 whose per-wave fp32 slabs fit the stages
+    constexpr int LDS_BYTES = 2 * (A_BYTES + B_BYTES);
+    constexpr int ER = (NW * 32 * EPS * 4 <= LDS_BYTES) ? 32 : (NW * 16 * EPS * 4 <= LDS_BYTES) ? 16 : 8;
+    static_assert(A_INSTR >= 1 && A_INSTR * NW * 1024 == A_BYTES, "X stage split");
+    static_assert(B_INSTR >= 1 && B_INSTR * NW * 1024 == B_BYTES, "W stage split");
+    static_assert(B_CPR >= 16 && B_CPR <= 64, "W swizzle needs 16..64 chunks per row");
+    static_assert(NW * ER * EPS * 4 <= LDS_BYTES, "epilogue slabs must fit the stage memory");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (A_ELEMS + B_ELEMS)];
+    // Two stages [X0 | W0 | X1 | W1]; the epilogue reuses the same memory.
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (A_BYTES + B_BYTES)];
+    typedef __attribute__((address_space(3))) uint8_t lds_t;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / NWN, wn = wave % NWN;
@@ -121,63 +154,65 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1)
     tile_of_block(p, blockIdx.x, rb, cb);
     const int64_t m0 = (int64_t)rb * BM, n0 = (int64_t)cb * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
-    const uint16_t *__restrict__ x = p.x;
-    const uint16_t *__restrict__ w = p.w;
 
-    uint4 ra[A_LD];
-    uint4 rw[B_LD][4];
+    // Buffer resources over X and W: a load whose offset is out of range
+    // returns zeros, which fills the M, N and K tails without branches.
+    const i32x4 xr = buffer_rsrc(p.x, (uint32_t)(M * K * 2));
+    const i32x4 wr = buffer_rsrc(p.w, (uint32_t)(K * N * 2));
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy for LDS bases
+    constexpr uint32_t kOob = 0x80000000u;
 
-    auto load_tile = [&](int64_t k0) {
+    // Per-lane source of each load.  X: instruction i covers 8 rows of the
+    // stage; lane -> (row, physical chunk) and loads the logical chunk the
+    // read-side swizzle expects.  W: instruction i covers B_RPI rows.  The
+    // per-lane byte offset is fixed for the whole K loop (rows/columns past M
+    // or N get an out-of-range offset); k0 goes into the scalar offset.
+    auto a_row_of = [&](int i) { return (wave * A_INSTR + i) * 8 + (lane >> 3); };
+    auto a_col_of = [&](int i) { return ((lane & 7) ^ swz_a(a_row_of(i))) * 8; };
+    auto b_row_of = [&](int i) { return (wave * B_INSTR + i) * B_RPI + lane / B_CPR; };
+    uint32_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int q = tid + i * NT;
-            const int64_t gm = m0 + (q >> 3), gk = k0 + (q & 7) * 8;
-            ra[i] = load16_or_zero(x + gm * K + gk, gm < M && gk < K);
+    for (int i = 0; i < A_INSTR; ++i) {
+        const int64_t gm = m0 + a_row_of(i);
+        a_off[i] = (gm < M) ? (uint32_t)((gm * K + a_col_of(i)) * 2) : kOob;
+    }
+#pragma unroll
+    for (int i = 0; i < B_INSTR; ++i) {
+        const int r = b_row_of(i);
+        const int64_t gn = n0 + ((lane % B_CPR) ^ swz_b(r)) * 8;
+        b_off[i] = (gn < N) ? (uint32_t)((r * N + gn) * 2) : kOob;
+    }
+
+    // Full K steps: offsets as precomputed, k0 in soffset.
+    auto lds_addr = [](const lds_t *ptr) { return (uint32_t)(uintptr_t)ptr; };
+    auto issue = [&](lds_t *As, lds_t *Bs, int64_t k0) {
+        const uint32_t sa = (uint32_t)(k0 * 2), sb = (uint32_t)(k0 * N * 2);
+        const uint32_t la = lds_addr(As) + wave_u * A_INSTR * 1024, lb = lds_addr(Bs) + wave_u * B_INSTR * 1024;
+#pragma unroll
+        for (int i = 0; i < A_INSTR; ++i) dma16(xr, la + i * 1024, a_off[i], sa);
+#pragma unroll
+        for (int i = 0; i < B_INSTR; ++i) dma16(wr, lb + i * 1024, b_off[i], sb);
+    };
+    // The last, partial K step: every lane checks its own k and zero-fills
+    // (out-of-range offset) what lies past K.
+    auto issue_tail = [&](lds_t *As, lds_t *Bs, int64_t k0) {
+        const uint32_t la = lds_addr(As) + wave_u * A_INSTR * 1024, lb = lds_addr(Bs) + wave_u * B_INSTR * 1024;
+#pragma unroll
+        for (int i = 0; i < A_INSTR; ++i) {
+            const bool in = a_off[i] != kOob && k0 + a_col_of(i) < K;
+            dma16(xr, la + i * 1024, in ? a_off[i] + (uint32_t)(k0 * 2) : kOob, 0);
         }
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int q = tid + i * NT;
-            const int kb4 = (q & 1) + 2 * ((q >> 1) / (BN / 8));
-            const int nb = (q >> 1) % (BN / 8);
-            const int64_t gn = n0 + nb * 8;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t gk = k0 + kb4 * 4 + j;
-                rw[i][j] = load16_or_zero(w + gk * N + gn, gk < K && gn < N);
-            }
+        for (int i = 0; i < B_INSTR; ++i) {
+            const bool in = b_off[i] != kOob && k0 + b_row_of(i) < K;
+            dma16(wr, lb + i * 1024, in ? b_off[i] + (uint32_t)(k0 * N * 2) : kOob, 0);
         }
     };
-
-    auto store_tile = [&](int buf) {
-        uint16_t *As = smem + buf * (A_ELEMS + B_ELEMS);
-        uint16_t *Bs = As + A_ELEMS;
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i) {
-            const int q = tid + i * NT;
-            *reinterpret_cast<uint4 *>(As + lds_off(q >> 3, q & 7)) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i) {
-            const int q = tid + i * NT;
-            const int kb4 = (q & 1) + 2 * ((q >> 1) / (BN / 8));
-            const int nb = (q >> 1) % (BN / 8);
-#pragma unroll
-            for (int jn = 0; jn < 8; ++jn) {
-                const int d = jn >> 1;
-                const uint32_t w0 = dword_of(rw[i][0], d), w1 = dword_of(rw[i][1], d);
-                const uint32_t w2 = dword_of(rw[i][2], d), w3 = dword_of(rw[i][3], d);
-                uint32_t lo, hi;
-                if (jn & 1) {
-                    lo = (w0 >> 16) | (w1 & 0xffff0000u);
-                    hi = (w2 >> 16) | (w3 & 0xffff0000u);
-                } else {
-                    lo = (w0 & 0xffffu) | (w1 << 16);
-                    hi = (w2 & 0xffffu) | (w3 << 16);
-                }
-                const int n = nb * 8 + jn;
-                *reinterpret_cast<uint2 *>(Bs + lds_off(n, kb4 >> 1) + (kb4 & 1) * 4) = make_uint2(lo, hi);
-            }
-        }
+    auto issue_step = [&](lds_t *As, lds_t *Bs, int64_t k0) {
+        if (k0 + BK <= K)
+            issue(As, Bs, k0);
+        else
+            issue_tail(As, Bs, k0);
     };
 
     f32x16 acc[TM][TN];
@@ -186,39 +221,98 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    auto compute = [&](int buf) {
-        const uint16_t *As = smem + buf * (A_ELEMS + B_ELEMS);
-        const uint16_t *Bs = As + A_ELEMS;
+    // MFMA operands: X rows with 16-byte swizzled reads; W columns with the
+    // gfx950 transpose read -- in each 16-lane group, lane (4a+b) receives
+    // element b of the 8-byte rows read by lanes a, a+4, a+8, a+12, so lanes
+    // that read 4 consecutive n of rows k..k+3 end up holding 4 consecutive k
+    // of one column, the B-operand layout.
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int b_n_lane = 16 * (g16 & 1) + 4 * (s16 & 3);  // n offset of this lane's 8-byte read
+    const int b_k_lane = 8 * (g16 >> 1) + (s16 >> 2);     // k offset (+4 for the upper half)
+    struct Frag {
+        bf16x8 a[TM], b[TN];
+    };
+    auto load_frag = [&](const lds_t *As, const lds_t *Bs, int kk, Frag &f) {
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int kc = kk * 2 + (lane >> 5);
-            bf16x8 a[TM], b[TN];
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * WM + i * 32 + (lane & 31);
+            const int c = kk * 2 + (lane >> 5);
+            f.a[i] = *(const __attribute__((address_space(3))) bf16x8 *)(As + r * (BK * 2) + ((c ^ swz_a(r)) << 4));
+        }
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-                a[i] = *reinterpret_cast<const bf16x8 *>(As + lds_off(wm * WM + i * 32 + (lane & 31), kc));
+        for (int j = 0; j < TN; ++j) {
+            const int n = wn * WN + j * 32 + b_n_lane;
+            bf16x4 h[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int k = kk * 16 + b_k_lane + 4 * half;
+                const lds_t *src = Bs + k * (BN * 2) + (((n >> 3) ^ swz_b(k)) << 4) + (n & 7) * 2;
+                h[half] = __builtin_bit_cast(
+                    bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)src));
+            }
+            f.b[j] = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    auto mma = [&](const Frag &f) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                b[j] = *reinterpret_cast<const bf16x8 *>(Bs + lds_off(wn * WN + j * 32 + (lane & 31), kc));
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
+    // Scheduling groups: after each MFMA one LDS operand read, so the reads of
+    // the next sub-step overlap the MFMAs of the current one (the compiler's
+    // default is to drain each read right before its first use).
+    constexpr int NREAD = TM + 2 * TN;  // LDS reads per sub-step
+    constexpr int NMMA = TM * TN;       // MFMAs per sub-step
+    constexpr int NK = BK / 16;         // MFMA sub-steps per K step
+    static_assert(NK % 2 == 0, "sub-step parity must repeat across K steps");
+    auto interleave = [&]() {
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int n = 0; n < NMMA; ++n) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // one MFMA
+            if (n < NREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
     };
 
-    // ---- mainloop ---------------------------------------------------------------
+    // ---- mainloop.  Step t computes from stage X = t%2 while the
+    // direct-to-LDS loads of step t+1 fill stage Y.  The pipeline is rotated
+    // across the barrier: sub-step 0's operands of step t were read right after
+    // the previous barrier, and the last sub-step's MFMAs of step t run after
+    // the barrier that publishes stage Y, overlapping the first operand reads
+    // of step t+1.  Before that barrier every wave has drained its loads of t+1
+    // (vmcnt) and its LDS reads of stage X (the barrier's lgkmcnt wait), so
+    // stage X can be refilled by step t+2.
+    lds_t *const S0 = (lds_t *)smem;
+    constexpr int STAGE = A_BYTES + B_BYTES;
     const int KT = (int)((K + BK - 1) / BK);
-    load_tile(0);
-    store_tile(0);
+    Frag f[2];
+    issue_step(S0, S0 + A_BYTES, 0);
+    wait_vmcnt_zero();
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const bool more = kt + 1 < KT;
-        if (more) load_tile((int64_t)(kt + 1) * BK);
-        compute(kt & 1);
-        if (more) store_tile((kt + 1) & 1);
+    load_frag(S0, S0 + A_BYTES, 0, f[0]);
+    for (int t = 0; t < KT; ++t) {
+        const lds_t *XA = S0 + (t & 1) * STAGE;
+        lds_t *YA = S0 + ((t + 1) & 1) * STAGE;
+        if (t + 1 < KT) issue_step(YA, YA + A_BYTES, (int64_t)(t + 1) * BK);
+#pragma unroll
+        for (int kk = 0; kk + 1 < NK; ++kk) {
+            load_frag(XA, XA + A_BYTES, kk + 1, f[(kk + 1) & 1]);
+            mma(f[kk & 1]);
+            interleave();
+        }
+        wait_vmcnt_zero();
         __syncthreads();
+        // (after the last step this reads stale operands that are never used)
+        load_frag(YA, YA + A_BYTES, 0, f[0]);
+        mma(f[(NK - 1) & 1]);
+        interleave();
     }
+    __syncthreads();  // the stages are reused by the epilogue below
+
+    // each wave stages its epilogue slabs in its own part of the (now idle) stages
+    float *const ep = reinterpret_cast<float *>(smem) + wave * ER * EPS;
+
 
     // ---- epilogue -----------------------------------------------------------------
     const bool sys = p.system_scope != 0;
@@ -255,54 +349,95 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1)
         __syncthreads();
     }
 
-    float *ep = reinterpret_cast<float *>(smem) + wave * 32 * EPS;
+    // Each wave drains its accumulators one ER-row slab at a time through its
+    // own LDS region (no workgroup barrier: a wave's LDS operations complete in
+    // order) and finishes row-contiguous 16-byte packs.  The peers' partials of
+    // owner rows are independent of the accumulators, so they are fetched D
+    // units ahead (a unit = one 16-byte pack per lane) with branch-free buffer
+    // loads; out-of-range and non-owner lanes use an out-of-range offset.
     constexpr int CPR = WN / 8;     // 16-byte chunks per epilogue row
-    constexpr int RPS = 64 / CPR;   // rows per step
-    constexpr int STEPS = 32 / RPS;
-    const int R = p.R, owner = p.owner;
+    constexpr int RPS = 64 / CPR;   // rows per unit
+    constexpr int STEPS = ER / RPS; // units per slab
+    constexpr int NQ = 32 / ER;     // slabs per 32-row MFMA block
+    constexpr int NU = TM * NQ * STEPS;
+    constexpr int kPeers = PEERS;       // peer slots compiled in (>= R - 1)
+    constexpr int DW = PEERS <= 3 ? 8 : 4;
+    constexpr int D = NU < DW ? NU : DW;  // prefetch depth in units
+    static_assert(STEPS >= 1 && STEPS * RPS == ER, "epilogue step split");
+    const uint32_t recv_bytes = (uint32_t)(p.seg * N * 2);
+    __amdgpu_buffer_rsrc_t prs[kPeers];
+    bool pvalid[kPeers];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int sl = 0; sl < kPeers; ++sl) {  // slots hold the peers in ascending rank order
+        pvalid[sl] = sl < p.npeers;
+        prs[sl] = __builtin_amdgcn_make_buffer_rsrc((void *)(pvalid[sl] ? p.peer[sl] : p.x), 0,
+                                                    pvalid[sl] ? (int)recv_bytes : 0, kBufferDword3);
+    }
+    auto unit_pos = [&](int u, int64_t &gr, int64_t &gc, int &row, int &ch) {
+        const int i = u / (NQ * STEPS), q = (u / STEPS) % NQ, st = u % STEPS;
+        row = st * RPS + lane / CPR;
+        ch = lane % CPR;
+        gr = m0 + wm * WM + i * 32 + q * ER + row;
+        gc = n0 + wn * WN + ch * 8;
+    };
+    auto prefetch = [&](int u, i32x4 (&pk)[kPeers]) {
+        int64_t gr, gc;
+        int row, ch;
+        unit_pos(u, gr, gc, row, ch);
+        const bool own = gr >= oseg0 && gr < oseg1 && gc < N;
+        const uint32_t off = own ? (uint32_t)(((gr - oseg0) * N + gc) * 2) : kOob;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int sl = 0; sl < kPeers; ++sl)
+            if (pvalid[sl]) pk[sl] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(prs[sl], off, 0, 0));
+    };
+    i32x4 pk[D][kPeers];
+    if (has_owner) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                ep[row * EPS + j * 32 + (lane & 31)] = acc[i][j][r];
-            }
-        __syncthreads();
+        for (int u = 0; u < D; ++u) prefetch(u, pk[u]);
+    }
 #pragma unroll
-        for (int st = 0; st < STEPS; ++st) {
-            const int row = st * RPS + lane / CPR, ch = lane % CPR;
-            const int64_t gr = m0 + wm * WM + i * 32 + row;
-            const int64_t gc = n0 + wn * WN + ch * 8;
-            if (gr < M && gc < N) {
-                const float4 v0 = *reinterpret_cast<const float4 *>(ep + row * EPS + ch * 8);
-                const float4 v1 = *reinterpret_cast<const float4 *>(ep + row * EPS + ch * 8 + 4);
-                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                if (gr >= oseg0 && gr < oseg1) {
-                    const int64_t off = (gr - oseg0) * N + gc;
+    for (int u = 0; u < NU; ++u) {
+        const int i = u / (NQ * STEPS), q = (u / STEPS) % NQ;
+        if (u % STEPS == 0) {
+            // accumulator register r of a 32x32 tile holds row 8*(r/4) + 4*(lane/32) + r%4
 #pragma unroll
-                    for (int pr = 0; pr < kMaxR; ++pr) {
-                        if (pr < R && pr != owner) {
-                            float f[8];
-                            unpack8(*reinterpret_cast<const uint4 *>(p.recv[pr] + off), f);
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] = v[e] + f[e];
-                        }
-                    }
-                    *reinterpret_cast<uint4 *>(p.out + off) = pack8(v);
-                } else if (p.send) {
-                    *reinterpret_cast<uint4 *>(p.send + gr * N + gc) = pack8(v);
+                for (int r = 0; r < 16; ++r) {
+                    const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    if (row / ER == q) ep[(row % ER) * EPS + j * 32 + (lane & 31)] = acc[i][j][r];
                 }
+        }
+        int64_t gr, gc;
+        int row, ch;
+        unit_pos(u, gr, gc, row, ch);
+        if (gr < M && gc < N) {
+            const float4 v0 = *reinterpret_cast<const float4 *>(ep + row * EPS + ch * 8);
+            const float4 v1 = *reinterpret_cast<const float4 *>(ep + row * EPS + ch * 8 + 4);
+            float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            if (gr >= oseg0 && gr < oseg1) {
+#pragma unroll
+                for (int sl = 0; sl < kPeers; ++sl) {
+                    if (pvalid[sl]) {
+                        float f[8];
+                        const i32x4 w4 = pk[u % D][sl];
+                        unpack8(make_uint4(w4.x, w4.y, w4.z, w4.w), f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = v[e] + f[e];
+                    }
+                }
+                *reinterpret_cast<uint4 *>(p.out + (gr - oseg0) * N + gc) = pack8(v);
+            } else if (p.send) {
+                *reinterpret_cast<uint4 *>(p.send + gr * N + gc) = pack8(v);
             }
         }
-        __syncthreads();
+        if (has_owner && u + D < NU) prefetch(u + D, pk[u % D]);
     }
 
     // Publish the send tiles: drain this thread's stores, balanced barrier, one
     // release, then relaxed bit sets.
     if (p.ready_out && has_other) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        drain_stores();
         __syncthreads();
         if (wave == 0) {
             fence_release(sys);
@@ -310,7 +445,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1)
             const int64_t tc0 = n0 / p.ftn, tc1 = (min(n0 + BN, N) - 1) / p.ftn;
             const int64_t ntc = tc1 - tc0 + 1;
             for (int64_t d = d0; d <= d1; ++d) {
-                if (d == owner) continue;
+                if (d == p.owner) continue;
                 const int64_t s0 = d * p.seg;
                 const int64_t lr0 = max(m0, s0) - s0, lr1 = min(m1, s0 + p.seg) - s0;
                 const int64_t tr0 = lr0 / p.ftm, tr1 = (lr1 - 1) / p.ftm;
@@ -375,8 +510,10 @@ int validate_shape(int64_t M, int64_t N, int64_t K, int R, int owner, int ftm, i
     if (K < 8 || K % 8) return bad("K=" + std::to_string(K) + " must be a positive multiple of 8");
     if (ftm < 1 || ftn < 1)
         return bad("flag tile " + std::to_string(ftm) + "x" + std::to_string(ftn) + " must be at least 1x1");
-    if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31))
-        return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: dimensions above 2^31 are not supported");
+    // X, W and each peer partial are addressed with 32-bit buffer offsets
+    const int64_t lim = int64_t(1) << 31;
+    if (M * K * 2 >= lim || K * N * 2 >= lim || (M / R) * N * 2 >= lim)
+        return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: X, W and each peer partial must be below 2 GiB");
     return AREPI_OK;
 }
 
@@ -399,7 +536,10 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool pub
 template <int BM, int BN, int WM, int WN>
 void launch(const GemmRsParams &p, hipStream_t stream) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
-    hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN>), dim3(p.nWG), dim3(NT), 0, stream, p);
+    if (p.npeers <= 3)
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, 3>), dim3(p.nWG), dim3(NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, kMaxR - 1>), dim3(p.nWG), dim3(NT), 0, stream, p);
 }
 
 }  // namespace
@@ -476,7 +616,9 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
     GemmRsParams p{};
     p.x = x;
     p.w = w;
-    for (int i = 0; i < kMaxR; ++i) p.recv[i] = (i < R && i != owner && recv) ? recv[i] : nullptr;
+    p.npeers = 0;
+    for (int i = 0; i < R; ++i)
+        if (i != owner) p.peer[p.npeers++] = recv[i];
     p.ready_in = ready_in;
     p.out = out;
     p.send = send;
