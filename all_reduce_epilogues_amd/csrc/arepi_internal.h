@@ -36,6 +36,23 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (nontemporal) 16-byte load/store: the nt cache policy, for data
+// touched once per kernel.
+__device__ __forceinline__ uint4 load16_nt(const void *p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store16_nt(void *p, uint4 v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
+
+// Cache-policy operand of the direct-to-LDS load builtins for a streaming
+// (nt) load on gfx950 (checked against the emitted assembly).
+constexpr int kAuxNontemporal = 2;
+
 // Two fp32 -> packed bf16x2 with round-to-nearest-even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2 v = {lo, hi};

@@ -16,7 +16,8 @@
 //
 // Work unit ("chunk"): one token t and 512 consecutive h (64 lanes x 8).  The
 // grid is a fixed set of single-wave workgroups (5 per CU: 32 KiB of LDS each
-// at E=8, S=4) looping over chunks with a grid stride.
+// at E=8, S=4) looping over chunks with a grid stride.  Expert rows are read
+// once, so the loads and the output stores are nontemporal (streaming).
 #include <string>
 
 #include "arepi_internal.h"
@@ -26,8 +27,6 @@ namespace {
 
 constexpr int kStages = 4;
 constexpr int kChunkH = 512;  // h values per chunk (64 lanes x 8)
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
     u32x4 v;
@@ -82,7 +81,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const uint16_t *__restrict_
         for (int k = 0; k < E; ++k)
             __builtin_amdgcn_global_load_lds(src + (int64_t)k * H,
                                              (__attribute__((address_space(3))) void *)(lds_stage(s) + k * 1024),
-                                             16, 0, 0);
+                                             16, 0, kAuxNontemporal);
     };
 
     for (int64_t i = 0; i < kStages - 1 && i < n_mine; ++i) issue(i);
@@ -110,7 +109,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const uint16_t *__restrict_
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[e] = acc[e] + g[k] * f[e];
         }
-        if (h < H) *reinterpret_cast<uint4 *>(out + t * H + h) = pack8(acc);
+        if (h < H) store16_nt(out + t * H + h, pack8(acc));
     }
 }
 

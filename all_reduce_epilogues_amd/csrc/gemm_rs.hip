@@ -71,10 +71,11 @@ constexpr int kBufferDword3 = 0x00020000;
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// X tile rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r sits at
-// c ^ ((r >> 1) & 7): 16 consecutive rows reading one logical chunk hit 16
-// distinct 16-byte bank groups (row parity x 8 chunks).
-__device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
+// X tile rows are BK*2 bytes (CH = BK/8 chunks of 16 bytes); chunk c of row r
+// sits at c ^ ((r / (16/CH)) % CH): the 16 consecutive rows that one 16-lane
+// group reads at one logical chunk hit 16 distinct 16-byte bank groups.
+template <int CH>
+__device__ __forceinline__ int swz_a(int r) { return (r / (16 / CH)) % CH; }
 // W tile rows are BN*2 bytes (BN/8 chunks); chunk c of row k sits at
 // c ^ (4 * (k & 3)): the four rows and four chunks one transpose read touches
 // per 16-lane group land in 16 distinct 16-byte bank groups.
@@ -84,6 +85,13 @@ __device__ __forceinline__ int swz_b(int k) { return 4 * (k & 3); }
 // moves memory operations across it).
 __device__ __forceinline__ void wait_vmcnt_zero() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void drain_stores() { wait_vmcnt_zero(); }
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and
+// lgkmcnt left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -124,28 +132,37 @@ __device__ __forceinline__ void tile_of_block(const GemmRsParams &p, int b, int 
     rb = (p.ob1 + pos) % p.nRB;  // rotated: owner row blocks come last
 }
 
-template <int BM, int BN, int WM, int WN, int PEERS>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// WPE: waves per SIMD the register allocation targets (1 = one big-tile
+// workgroup per CU; 2 = two co-resident workgroups; 0 = no target).
+template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+    __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, WPE > 0 ? WPE : 8)))
     gemm_rs_kernel(const GemmRsParams p) {
     constexpr int NWN = BN / WN;
     constexpr int NW = (BM / WM) * NWN;
     constexpr int TM = WM / 32, TN = WN / 32;
+    constexpr int CH = BK / 8;                    // 16-byte chunks per X row in LDS
     constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * BN * 2;  // one stage
-    constexpr int A_INSTR = A_BYTES / 1024 / NW;  // 1 KiB direct-to-LDS loads per wave
+    constexpr int A_INSTR = A_BYTES / 1024 / NW;  // 1 KiB direct-to-LDS loads per wave and step
     constexpr int B_INSTR = B_BYTES / 1024 / NW;
+    constexpr int NDMA = A_INSTR + B_INSTR;
+    constexpr int A_RPI = 64 / CH;                // X rows per load instruction
     constexpr int B_CPR = BN / 8;                 // 16-byte chunks per W row in LDS
     constexpr int B_RPI = 64 / B_CPR;             // W rows per load instruction
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int LDS_BYTES = S * STAGE;
     constexpr int EPS = WN + 8;                   // epilogue LDS row stride (floats)
     // epilogue slab rows: the largest of 32/16/8 whose per-wave fp32 slabs fit the stages
-    constexpr int LDS_BYTES = 2 * (A_BYTES + B_BYTES);
     constexpr int ER = (NW * 32 * EPS * 4 <= LDS_BYTES) ? 32 : (NW * 16 * EPS * 4 <= LDS_BYTES) ? 16 : 8;
+    static_assert(CH == 4 || CH == 8, "BK must be 32 or 64");
     static_assert(A_INSTR >= 1 && A_INSTR * NW * 1024 == A_BYTES, "X stage split");
     static_assert(B_INSTR >= 1 && B_INSTR * NW * 1024 == B_BYTES, "W stage split");
     static_assert(B_CPR >= 16 && B_CPR <= 64, "W swizzle needs 16..64 chunks per row");
     static_assert(NW * ER * EPS * 4 <= LDS_BYTES, "epilogue slabs must fit the stage memory");
+    static_assert(S >= 2 && (S - 2) * NDMA < 64, "stage count vs vmcnt range");
 
-    // Two stages [X0 | W0 | X1 | W1]; the epilogue reuses the same memory.
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * (A_BYTES + B_BYTES)];
+    // S stages [X | W] x S; the epilogue reuses the same memory.
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
     typedef __attribute__((address_space(3))) uint8_t lds_t;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -162,13 +179,13 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy for LDS bases
     constexpr uint32_t kOob = 0x80000000u;
 
-    // Per-lane source of each load.  X: instruction i covers 8 rows of the
+    // Per-lane source of each load.  X: instruction i covers A_RPI rows of the
     // stage; lane -> (row, physical chunk) and loads the logical chunk the
     // read-side swizzle expects.  W: instruction i covers B_RPI rows.  The
     // per-lane byte offset is fixed for the whole K loop (rows/columns past M
     // or N get an out-of-range offset); k0 goes into the scalar offset.
-    auto a_row_of = [&](int i) { return (wave * A_INSTR + i) * 8 + (lane >> 3); };
-    auto a_col_of = [&](int i) { return ((lane & 7) ^ swz_a(a_row_of(i))) * 8; };
+    auto a_row_of = [&](int i) { return (wave * A_INSTR + i) * A_RPI + lane / CH; };
+    auto a_col_of = [&](int i) { return ((lane % CH) ^ swz_a<CH>(a_row_of(i))) * 8; };
     auto b_row_of = [&](int i) { return (wave * B_INSTR + i) * B_RPI + lane / B_CPR; };
     uint32_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
@@ -183,37 +200,39 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((
         b_off[i] = (gn < N) ? (uint32_t)((r * N + gn) * 2) : kOob;
     }
 
-    // Full K steps: offsets as precomputed, k0 in soffset.
+    lds_t *const S0 = (lds_t *)smem;
     auto lds_addr = [](const lds_t *ptr) { return (uint32_t)(uintptr_t)ptr; };
-    auto issue = [&](lds_t *As, lds_t *Bs, int64_t k0) {
-        const uint32_t sa = (uint32_t)(k0 * 2), sb = (uint32_t)(k0 * N * 2);
-        const uint32_t la = lds_addr(As) + wave_u * A_INSTR * 1024, lb = lds_addr(Bs) + wave_u * B_INSTR * 1024;
+    const int KT = (int)((K + BK - 1) / BK);
+    // Loads of K step kt into stage kt % S.  Every call issues exactly NDMA
+    // instructions per wave (steps past the end load nothing but zeros, with
+    // out-of-range offsets) so the vmcnt arithmetic below is uniform.
+    auto issue_step = [&](int kt) {
+        const lds_t *st = S0 + (kt % S) * STAGE;
+        const uint32_t la = lds_addr(st) + wave_u * A_INSTR * 1024;
+        const uint32_t lb = lds_addr(st + A_BYTES) + wave_u * B_INSTR * 1024;
+        const int64_t k0 = (int64_t)kt * BK;
+        if (k0 + BK <= K) {  // full step: precomputed offsets, k0 in soffset
+            const uint32_t sa = (uint32_t)(k0 * 2), sb = (uint32_t)(k0 * N * 2);
 #pragma unroll
-        for (int i = 0; i < A_INSTR; ++i) dma16(xr, la + i * 1024, a_off[i], sa);
+            for (int i = 0; i < A_INSTR; ++i) dma16(xr, la + i * 1024, a_off[i], sa);
 #pragma unroll
-        for (int i = 0; i < B_INSTR; ++i) dma16(wr, lb + i * 1024, b_off[i], sb);
-    };
-    // The last, partial K step: every lane checks its own k and zero-fills
-    // (out-of-range offset) what lies past K.
-    auto issue_tail = [&](lds_t *As, lds_t *Bs, int64_t k0) {
-        const uint32_t la = lds_addr(As) + wave_u * A_INSTR * 1024, lb = lds_addr(Bs) + wave_u * B_INSTR * 1024;
+            for (int i = 0; i < B_INSTR; ++i) dma16(wr, lb + i * 1024, b_off[i], sb);
+        } else {  // partial or past-the-end step: every lane checks its own k
 #pragma unroll
-        for (int i = 0; i < A_INSTR; ++i) {
-            const bool in = a_off[i] != kOob && k0 + a_col_of(i) < K;
-            dma16(xr, la + i * 1024, in ? a_off[i] + (uint32_t)(k0 * 2) : kOob, 0);
+            for (int i = 0; i < A_INSTR; ++i) {
+                const bool in = a_off[i] != kOob && k0 + a_col_of(i) < K;
+                dma16(xr, la + i * 1024, in ? a_off[i] + (uint32_t)(k0 * 2) : kOob, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < B_INSTR; ++i) {
+                const bool in = b_off[i] != kOob && k0 + b_row_of(i) < K;
+                dma16(wr, lb + i * 1024, in ? b_off[i] + (uint32_t)(k0 * N * 2) : kOob, 0);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < B_INSTR; ++i) {
-            const bool in = b_off[i] != kOob && k0 + b_row_of(i) < K;
-            dma16(wr, lb + i * 1024, in ? b_off[i] + (uint32_t)(k0 * N * 2) : kOob, 0);
-        }
     };
-    auto issue_step = [&](lds_t *As, lds_t *Bs, int64_t k0) {
-        if (k0 + BK <= K)
-            issue(As, Bs, k0);
-        else
-            issue_tail(As, Bs, k0);
-    };
+    // wait until this wave's loads of the oldest outstanding step have landed,
+    // leaving the S-2 younger steps in flight
+    auto wait_oldest_step = [&]() { wait_vmcnt<(S - 2) * NDMA>(); };
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -232,12 +251,13 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((
     struct Frag {
         bf16x8 a[TM], b[TN];
     };
-    auto load_frag = [&](const lds_t *As, const lds_t *Bs, int kk, Frag &f) {
+    auto load_frag = [&](const lds_t *As, int kk, Frag &f) {
+        const lds_t *Bs = As + A_BYTES;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int r = wm * WM + i * 32 + (lane & 31);
             const int c = kk * 2 + (lane >> 5);
-            f.a[i] = *(const __attribute__((address_space(3))) bf16x8 *)(As + r * (BK * 2) + ((c ^ swz_a(r)) << 4));
+            f.a[i] = *(const __attribute__((address_space(3))) bf16x8 *)(As + r * (BK * 2) + ((c ^ swz_a<CH>(r)) << 4));
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -275,44 +295,42 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((
         }
     };
 
-    // ---- mainloop.  Step t computes from stage X = t%2 while the
-    // direct-to-LDS loads of step t+1 fill stage Y.  The pipeline is rotated
-    // across the barrier: sub-step 0's operands of step t were read right after
-    // the previous barrier, and the last sub-step's MFMAs of step t run after
-    // the barrier that publishes stage Y, overlapping the first operand reads
-    // of step t+1.  Before that barrier every wave has drained its loads of t+1
-    // (vmcnt) and its LDS reads of stage X (the barrier's lgkmcnt wait), so
-    // stage X can be refilled by step t+2.
-    lds_t *const S0 = (lds_t *)smem;
-    constexpr int STAGE = A_BYTES + B_BYTES;
-    const int KT = (int)((K + BK - 1) / BK);
+    // ---- mainloop: an S-stage ring.  Step t computes from stage t%S while the
+    // loads of steps t+1..t+S-1 are in flight; at its top it issues step
+    // t+S-1 into the stage step t-1 used (free since the barrier that ended
+    // step t-1).  The pipeline is rotated across the barrier: sub-step 0's
+    // operands of step t were read right after the previous barrier, and the
+    // last sub-step's MFMAs of step t run after the barrier that publishes step
+    // t+1, overlapping its first operand reads.  Before that barrier every wave
+    // has its own loads of step t+1 landed (vmcnt) and its LDS reads of stage
+    // t%S done (the barrier's lgkmcnt wait).
     Frag f[2];
-    issue_step(S0, S0 + A_BYTES, 0);
-    wait_vmcnt_zero();
+#pragma unroll
+    for (int s0 = 0; s0 < S - 1; ++s0) issue_step(s0);
+    wait_oldest_step();
     __syncthreads();
-    load_frag(S0, S0 + A_BYTES, 0, f[0]);
+    load_frag(S0, 0, f[0]);
     for (int t = 0; t < KT; ++t) {
-        const lds_t *XA = S0 + (t & 1) * STAGE;
-        lds_t *YA = S0 + ((t + 1) & 1) * STAGE;
-        if (t + 1 < KT) issue_step(YA, YA + A_BYTES, (int64_t)(t + 1) * BK);
+        const lds_t *X = S0 + (t % S) * STAGE;
+        issue_step(t + S - 1);
 #pragma unroll
         for (int kk = 0; kk + 1 < NK; ++kk) {
-            load_frag(XA, XA + A_BYTES, kk + 1, f[(kk + 1) & 1]);
+            load_frag(X, kk + 1, f[(kk + 1) & 1]);
             mma(f[kk & 1]);
             interleave();
         }
-        wait_vmcnt_zero();
+        wait_oldest_step();
         __syncthreads();
-        // (after the last step this reads stale operands that are never used)
-        load_frag(YA, YA + A_BYTES, 0, f[0]);
+        // (after the last step this reads operands that are never used)
+        load_frag(S0 + ((t + 1) % S) * STAGE, 0, f[0]);
         mma(f[(NK - 1) & 1]);
         interleave();
     }
+    wait_vmcnt_zero();
     __syncthreads();  // the stages are reused by the epilogue below
 
     // each wave stages its epilogue slabs in its own part of the (now idle) stages
     float *const ep = reinterpret_cast<float *>(smem) + wave * ER * EPS;
-
 
     // ---- epilogue -----------------------------------------------------------------
     const bool sys = p.system_scope != 0;
@@ -361,7 +379,7 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((
     constexpr int NQ = 32 / ER;     // slabs per 32-row MFMA block
     constexpr int NU = TM * NQ * STEPS;
     constexpr int kPeers = PEERS;       // peer slots compiled in (>= R - 1)
-    constexpr int DW = PEERS <= 3 ? 8 : 4;
+    constexpr int DW = WPE != 1 ? (PEERS <= 3 ? 4 : 2) : (PEERS <= 3 ? 8 : 4);
     constexpr int D = NU < DW ? NU : DW;  // prefetch depth in units
     static_assert(STEPS >= 1 && STEPS * RPS == ER, "epilogue step split");
     const uint32_t recv_bytes = (uint32_t)(p.seg * N * 2);
@@ -388,7 +406,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((
         const uint32_t off = own ? (uint32_t)(((gr - oseg0) * N + gc) * 2) : kOob;
 #pragma unroll
         for (int sl = 0; sl < kPeers; ++sl)
-            if (pvalid[sl]) pk[sl] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(prs[sl], off, 0, 0));
+            if (pvalid[sl])
+                pk[sl] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(prs[sl], off, 0, kAuxNontemporal));
     };
     i32x4 pk[D][kPeers];
     if (has_owner) {
@@ -426,9 +445,9 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((
                         for (int e = 0; e < 8; ++e) v[e] = v[e] + f[e];
                     }
                 }
-                *reinterpret_cast<uint4 *>(p.out + (gr - oseg0) * N + gc) = pack8(v);
+                store16_nt(p.out + (gr - oseg0) * N + gc, pack8(v));
             } else if (p.send) {
-                *reinterpret_cast<uint4 *>(p.send + gr * N + gc) = pack8(v);
+                store16_nt(p.send + gr * N + gc, pack8(v));
             }
         }
         if (has_owner && u + D < NU) prefetch(u + D, pk[u % D]);
@@ -464,14 +483,21 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64, 1) __attribute__((
 
 struct TileCfg {
     int id, BM, BN;
+    int slots;   // workgroups co-resident on one CU (LDS / register bound)
     double eff;  // relative per-CU throughput used by the automatic choice
 };
+// eff: sustained per-CU throughput relative to the best tile, from timing the
+// tp=4 / tp=8 workloads on MI355X; cost = waves of tiles x tile area / eff.
 constexpr TileCfg kTiles[] = {
-    {AREPI_TILE_256x256, 256, 256, 1.00},
-    {AREPI_TILE_128x256, 128, 256, 0.92},
-    {AREPI_TILE_128x128, 128, 128, 0.80},
-    {AREPI_TILE_64x128, 64, 128, 0.55},
-    {AREPI_TILE_32x256, 32, 256, 0.50},
+    {AREPI_TILE_256x256_S4, 256, 256, 1, 1.00},
+    {AREPI_TILE_128x256_S3, 128, 256, 2, 0.98},
+    {AREPI_TILE_256x128_S3, 256, 128, 2, 0.97},
+    {AREPI_TILE_256x256, 256, 256, 1, 0.93},
+    {AREPI_TILE_128x128_S4, 128, 128, 2, 0.82},
+    {AREPI_TILE_128x256, 128, 256, 1, 0.80},
+    {AREPI_TILE_128x128, 128, 128, 2, 0.75},
+    {AREPI_TILE_64x128, 64, 128, 3, 0.60},
+    {AREPI_TILE_32x256, 32, 256, 2, 0.40},
 };
 
 const TileCfg *find_tile(int id) {
@@ -524,7 +550,8 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool pub
     for (const auto &t : kTiles) {
         if (publish && !flags_nest(M, N, R, ftm, ftn, t.BM, t.BN)) continue;
         const int64_t count = cdiv(M, t.BM) * cdiv(N, t.BN);
-        const double cost = (double)cdiv(count, 256) * t.BM * t.BN / t.eff;
+        // waves of co-resident tiles x work per CU per wave / efficiency
+        const double cost = (double)cdiv(count, 256 * t.slots) * t.slots * t.BM * t.BN / t.eff;
         if (best < 0 || cost < best_cost) {
             best = t.id;
             best_cost = cost;
@@ -533,13 +560,14 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool pub
     return best;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int BK, int S, int WPE>
 void launch(const GemmRsParams &p, hipStream_t stream) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
     if (p.npeers <= 3)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, 3>), dim3(p.nWG), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3>), dim3(p.nWG), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, kMaxR - 1>), dim3(p.nWG), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1>), dim3(p.nWG), dim3(NT), 0,
+                           stream, p);
 }
 
 }  // namespace
@@ -648,11 +676,15 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (cfg) {
-        case AREPI_TILE_256x256: launch<256, 256, 128, 128>(p, s); break;
-        case AREPI_TILE_128x256: launch<128, 256, 64, 128>(p, s); break;
-        case AREPI_TILE_128x128: launch<128, 128, 64, 64>(p, s); break;
-        case AREPI_TILE_64x128: launch<64, 128, 32, 64>(p, s); break;
-        case AREPI_TILE_32x256: launch<32, 256, 32, 64>(p, s); break;
+        case AREPI_TILE_256x256: launch<256, 256, 128, 128, 64, 2, 1>(p, s); break;
+        case AREPI_TILE_128x256: launch<128, 256, 64, 128, 64, 2, 1>(p, s); break;
+        case AREPI_TILE_128x128: launch<128, 128, 64, 64, 64, 2, 0>(p, s); break;
+        case AREPI_TILE_64x128: launch<64, 128, 32, 64, 64, 2, 0>(p, s); break;
+        case AREPI_TILE_32x256: launch<32, 256, 32, 64, 64, 2, 0>(p, s); break;
+        case AREPI_TILE_256x256_S4: launch<256, 256, 128, 128, 32, 4, 1>(p, s); break;
+        case AREPI_TILE_256x128_S3: launch<256, 128, 128, 64, 32, 3, 2>(p, s); break;
+        case AREPI_TILE_128x256_S3: launch<128, 256, 64, 128, 32, 3, 2>(p, s); break;
+        case AREPI_TILE_128x128_S4: launch<128, 128, 64, 64, 32, 4, 2>(p, s); break;
         default: return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_fused: no kernel for tile " + std::to_string(cfg));
     }
     return check_launch("arepi_gemm_rs_fused");

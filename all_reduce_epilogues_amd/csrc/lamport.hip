@@ -11,11 +11,11 @@
 //     is 0x8000, consumes it and re-arms it (each pack has exactly one consumer
 //     thread, so the re-arm needs no extra synchronisation).
 //
-// gfx950 mapping: the publisher's stores and the consumer's polls and re-arm
-// stores are device-coherent 8-byte atomics (relaxed, agent or system scope),
-// which the compiler lowers to sc1 global loads/stores: they are not served
-// from an XCD's non-coherent L2 copy, so a pack written from another XCD is
-// seen, and a re-arm can never be written back over a later publication.
+// gfx950 mapping: the publisher's stores are device-coherent 8-byte atomics
+// (relaxed, agent or system scope; the compiler emits sc1 stores), so a
+// consumer polling from another XCD sees them while the publisher runs.  The
+// consumer reads each pack once with a plain 16-byte load and only polls
+// coherently (sc1 loads) when the pack still shows a sentinel.
 //
 // Consumer layout: one 256-thread workgroup per row; thread t owns packs
 // t, t+256, ... of the row (coalesced 16-byte columns), keeps the fp32 slot sums
@@ -80,6 +80,15 @@ __global__ void __launch_bounds__(256) publish_kernel(const uint16_t *__restrict
     }
 }
 
+// Consumer.  First pass over a row: one plain 16-byte load per (pack, slot).
+// A kernel launch is an acquire at agent scope, so inside this launch a plain
+// load returns either the sentinel or data published during the launch -- never
+// an older payload.  Staging is touched once per launch, so these loads, the
+// re-arm stores and the output stores are nontemporal (streaming).  Packs that still show a sentinel are polled again with
+// device-coherent loads (which observe a producer running concurrently on
+// another XCD) until they land or the spin budget runs out.  Re-arm and output
+// are plain 16-byte stores; the kernel end releases them before any later
+// publication into the same staging.
 template <int PPT>
 __global__ void __launch_bounds__(256) ar_rmsnorm_kernel(uint16_t *__restrict__ staging,
                                                         const uint16_t *__restrict__ gamma,
@@ -90,51 +99,60 @@ __global__ void __launch_bounds__(256) ar_rmsnorm_kernel(uint16_t *__restrict__ 
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const int64_t packs = N / 8;
-    const int64_t plane = M * N;
+    const int64_t plane = M * N;  // elements per slot
     const bool sys = system != 0;
     float s[PPT][8];
     float ss = 0.f;
     int64_t spins = 0;
     bool gave_up = false;
+    const uint4 armed = make_uint4(kSent2, kSent2, kSent2, kSent2);
 
+    // Two-deep pipeline over this thread's packs: the S slot loads of pack j+1
+    // are in flight while pack j is checked, summed and re-armed.
+    uint4 q[2][8];
+    auto issue = [&](int j, uint4 (&d)[8]) {
+        const int64_t pk = tid + (int64_t)j * 256;
+        const uint16_t *base = staging + row * N + (pk < packs ? pk : 0) * 8;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl)
+            if (sl < S && pk < packs) d[sl] = load16_nt(base + sl * plane);
+    };
+    issue(0, q[0]);
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
+        if (j + 1 < PPT) issue(j + 1, q[(j + 1) & 1]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[j][e] = 0.f;
         const int64_t pk = tid + (int64_t)j * 256;
         if (pk < packs) {
-            uint64_t *base = reinterpret_cast<uint64_t *>(staging + row * N + pk * 8);
-            uint64_t lo[8], hi[8];
+            uint16_t *base = staging + row * N + pk * 8;
 #pragma unroll
             for (int sl = 0; sl < 8; ++sl) {
                 if (sl < S) {
-                    lo[sl] = load64_coherent(base + sl * (plane / 4), sys);
-                    hi[sl] = load64_coherent(base + sl * (plane / 4) + 1, sys);
-                }
-            }
-#pragma unroll
-            for (int sl = 0; sl < 8; ++sl) {
-                if (sl < S) {
-                    // spin until the pack has landed (bounded)
-                    while (!gave_up && (has_sentinel(lo[sl]) || has_sentinel(hi[sl]))) {
-                        if (++spins > spin_limit) {
-                            gave_up = true;
-                            if (status) atomicOr(status, (uint32_t)AREPI_STATUS_TIMEOUT);
-                            break;
+                    uint64_t lo = (uint64_t)q[j & 1][sl].x | ((uint64_t)q[j & 1][sl].y << 32);
+                    uint64_t hi = (uint64_t)q[j & 1][sl].z | ((uint64_t)q[j & 1][sl].w << 32);
+                    if (has_sentinel(lo) || has_sentinel(hi)) {
+                        // not (fully) landed yet: bounded coherent polling
+                        uint64_t *p64 = reinterpret_cast<uint64_t *>(base + sl * plane);
+                        while (!gave_up) {
+                            lo = load64_coherent(p64, sys);
+                            hi = load64_coherent(p64 + 1, sys);
+                            if (!has_sentinel(lo) && !has_sentinel(hi)) break;
+                            if (++spins > spin_limit) {
+                                gave_up = true;
+                                if (status) atomicOr(status, (uint32_t)AREPI_STATUS_TIMEOUT);
+                                break;
+                            }
+                            __builtin_amdgcn_s_sleep(2);
                         }
-                        __builtin_amdgcn_s_sleep(2);
-                        lo[sl] = load64_coherent(base + sl * (plane / 4), sys);
-                        hi[sl] = load64_coherent(base + sl * (plane / 4) + 1, sys);
                     }
-                    const uint4 q = make_uint4((uint32_t)lo[sl], (uint32_t)(lo[sl] >> 32), (uint32_t)hi[sl],
-                                               (uint32_t)(hi[sl] >> 32));
+                    const uint4 v = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
                     float f[8];
-                    unpack8(q, f);
+                    unpack8(v, f);
 #pragma unroll
                     for (int e = 0; e < 8; ++e) s[j][e] = s[j][e] + f[e];
                     // re-arm the consumed pack
-                    store64_coherent(base + sl * (plane / 4), kSent4, sys);
-                    store64_coherent(base + sl * (plane / 4) + 1, kSent4, sys);
+                    store16_nt(base + sl * plane, armed);
                 }
             }
 #pragma unroll
@@ -157,7 +175,7 @@ __global__ void __launch_bounds__(256) ar_rmsnorm_kernel(uint16_t *__restrict__ 
             unpack8(g, gf);
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] = (s[j][e] * r) * gf[e];
-            *reinterpret_cast<uint4 *>(out + row * N + pk * 8) = pack8(y);
+            store16_nt(out + row * N + pk * 8, pack8(y));
         }
     }
 }

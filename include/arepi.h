@@ -54,14 +54,20 @@ enum { AREPI_SCOPE_AGENT = 0, AREPI_SCOPE_SYSTEM = 1 };
 /* Bits ORed into a device status word. */
 enum { AREPI_STATUS_TIMEOUT = 1u };
 
-/* Compute-tile choice for arepi_gemm_rs_fused (0 = chosen from the shape). */
+/* Compute-tile choice for arepi_gemm_rs_fused (0 = chosen from the shape).
+ * BMxBN is the output tile of one workgroup; the _S variants walk K in
+ * 32-wide steps through an S-stage LDS ring (the others: 64-wide, 2 stages). */
 enum {
     AREPI_TILE_AUTO = 0,
     AREPI_TILE_256x256 = 1,
     AREPI_TILE_128x256 = 2,
     AREPI_TILE_128x128 = 3,
     AREPI_TILE_64x128 = 4,
-    AREPI_TILE_32x256 = 5
+    AREPI_TILE_32x256 = 5,
+    AREPI_TILE_256x256_S4 = 6,
+    AREPI_TILE_256x128_S3 = 7,
+    AREPI_TILE_128x256_S3 = 8,
+    AREPI_TILE_128x128_S4 = 9
 };
 
 /* Message describing the last failed call on this thread ("" if none). */

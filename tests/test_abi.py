@@ -54,8 +54,7 @@ def nests(M, N, R, ftm, ftn, BM, BN):
     return True
 
 
-TILE_DIMS = {A.TILE_256x256: (256, 256), A.TILE_128x256: (128, 256), A.TILE_128x128: (128, 128),
-             A.TILE_64x128: (64, 128), A.TILE_32x256: (32, 256)}
+TILE_DIMS = A.TILE_DIMS
 
 
 @pytest.mark.parametrize("M,N,R,ftm,ftn", [

@@ -70,7 +70,7 @@ def check_against_oracle(case, res, ftm=128, ftn=128, rows=None, what=""):
 
 
 def tiles_to_try(case, ftm, ftn):
-    for t in (A.TILE_256x256, A.TILE_128x256, A.TILE_128x128, A.TILE_64x128, A.TILE_32x256):
+    for t in sorted(A.TILE_NAMES):
         pub = A.gemm_rs_supports(case["M"], case["N"], case["K"], case["R"], case["owner"], ftm, ftn,
                                  publish=True, tile=t) == 0
         yield t, pub
