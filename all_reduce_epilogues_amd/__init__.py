@@ -8,7 +8,8 @@ raises if ``libarepi.so`` is missing or a kernel launch is refused.
 
 Names mirror the C entry points without the ``arepi_`` prefix:
   gemm_rs_fused, gemm_rs_supports, gemm_rs_flag_words, gemm_rs_pick_tile,
-  lamport_prefill, lamport_publish, ar_rmsnorm_lamport, combine_reduce,
+  lamport_prefill, lamport_publish, ar_rmsnorm_lamport, combine_reduce (and its
+  LDS-staged variant via pipeline="lds"),
   emu_peer_producer, last_error, version.
 """
 from __future__ import annotations
@@ -67,6 +68,7 @@ def lib():
             "arepi_lamport_publish": ([vp, vp, vp, i32, i64, i64, i32, i32, i32, vp], i32),
             "arepi_ar_rmsnorm_lamport": ([vp, vp, vp, i64, i64, i32, f32, i32, u32p, i64, vp], i32),
             "arepi_combine_reduce": ([vp, vp, vp, i64, i32, i64, vp], i32),
+            "arepi_combine_reduce_lds": ([vp, vp, vp, i64, i32, i64, vp], i32),
             "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp], i32),
         }
         for name, (args, res) in sig.items():
@@ -246,11 +248,18 @@ def ar_rmsnorm_lamport(staging, gamma, out, eps: float = 1e-6, scope: int = SCOP
 
 # ---- combine --------------------------------------------------------------------------
 
-def combine_reduce(x, gate, out, stream=None):
+def combine_reduce(x, gate, out, stream=None, pipeline: str = "registers"):
+    """out[t,h] = bf16(sum_k gate[t,k] * x[t,k,h]).  pipeline="lds" selects the
+    LDS-staged kernel (arepi_combine_reduce_lds) instead of the default."""
     _bf16(x, "x")
     T, E, H = x.shape
     torch = _torch()
     _need(gate, "gate", (torch.float32,), (T, E))
     _bf16(out, "out", (T, H))
-    _check(lib().arepi_combine_reduce(_ptr(x), _ptr(gate), _ptr(out), T, E, H, _stream(stream)),
-           "combine_reduce")
+    if pipeline == "registers":
+        fn, name = lib().arepi_combine_reduce, "combine_reduce"
+    elif pipeline == "lds":
+        fn, name = lib().arepi_combine_reduce_lds, "combine_reduce_lds"
+    else:
+        raise ValueError("pipeline must be 'registers' or 'lds'")
+    _check(fn(_ptr(x), _ptr(gate), _ptr(out), T, E, H, _stream(stream)), name)

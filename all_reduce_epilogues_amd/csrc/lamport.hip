@@ -17,10 +17,12 @@
 // consumer reads each pack once with a plain 16-byte load and only polls
 // coherently (sc1 loads) when the pack still shows a sentinel.
 //
-// Consumer layout: one 256-thread workgroup per row; thread t owns packs
-// t, t+256, ... of the row (coalesced 16-byte columns), keeps the fp32 slot sums
-// of its packs in registers, reduces sum(s^2) across the workgroup (wave
-// shuffles, then LDS), and writes the normalised row.
+// Consumer layout: one 256-thread workgroup per row; thread t owns packs t,
+// t+256, ... of the row (coalesced 16-byte columns; 3-4 each at N=7168), keeps
+// the fp32 slot sums of its packs in registers, reduces sum(s^2) across the
+// workgroup (wave shuffles, then LDS), and writes the normalised row.  (Two-
+// and eight-wave rows, persistent row loops and a slot-interleaved staging
+// layout all measured slower or equal on MI355X.)
 #include <string>
 
 #include "arepi_internal.h"
@@ -89,13 +91,14 @@ __global__ void __launch_bounds__(256) publish_kernel(const uint16_t *__restrict
 // another XCD) until they land or the spin budget runs out.  Re-arm and output
 // are plain 16-byte stores; the kernel end releases them before any later
 // publication into the same staging.
-template <int PPT>
-__global__ void __launch_bounds__(256) ar_rmsnorm_kernel(uint16_t *__restrict__ staging,
+// NT threads per row: two waves up to 1024 packs (N <= 8192), four above.
+template <int PPT, int NT>
+__global__ void __launch_bounds__(NT) ar_rmsnorm_kernel(uint16_t *__restrict__ staging,
                                                         const uint16_t *__restrict__ gamma,
                                                         uint16_t *__restrict__ out, int64_t M,
                                                         int64_t N, int S, float eps, int system,
                                                         uint32_t *status, int64_t spin_limit) {
-    __shared__ float red[4];
+    __shared__ float red[NT / 64];
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const int64_t packs = N / 8;
@@ -111,7 +114,7 @@ __global__ void __launch_bounds__(256) ar_rmsnorm_kernel(uint16_t *__restrict__ 
     // are in flight while pack j is checked, summed and re-armed.
     uint4 q[2][8];
     auto issue = [&](int j, uint4 (&d)[8]) {
-        const int64_t pk = tid + (int64_t)j * 256;
+        const int64_t pk = tid + (int64_t)j * NT;
         const uint16_t *base = staging + row * N + (pk < packs ? pk : 0) * 8;
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl)
@@ -123,7 +126,7 @@ __global__ void __launch_bounds__(256) ar_rmsnorm_kernel(uint16_t *__restrict__ 
         if (j + 1 < PPT) issue(j + 1, q[(j + 1) & 1]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[j][e] = 0.f;
-        const int64_t pk = tid + (int64_t)j * 256;
+        const int64_t pk = tid + (int64_t)j * NT;
         if (pk < packs) {
             uint16_t *base = staging + row * N + pk * 8;
 #pragma unroll
@@ -164,11 +167,13 @@ __global__ void __launch_bounds__(256) ar_rmsnorm_kernel(uint16_t *__restrict__ 
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
-    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    float tot = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) tot = tot + red[w];
     const float r = 1.0f / sqrtf(tot / (float)N + eps);
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-        const int64_t pk = tid + (int64_t)j * 256;
+        const int64_t pk = tid + (int64_t)j * NT;
         if (pk < packs) {
             const uint4 g = *reinterpret_cast<const uint4 *>(gamma + pk * 8);
             float gf[8], y[8];
@@ -238,21 +243,21 @@ extern "C" int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma
         return bad("staging, gamma and out must be 16-byte aligned");
     if (M > (int64_t)1 << 31) return fail(AREPI_EUNSUPPORTED, "arepi_ar_rmsnorm_lamport: M above 2^31");
     const int64_t packs = N / 8;
-    const int ppt = (int)((packs + 255) / 256);
     const int64_t lim = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
     const int sys = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int ppt = (int)((packs + 255) / 256);
+#define AREPI_RMS_LAUNCH(P, T)                                                                                   \
+    hipLaunchKernelGGL((ar_rmsnorm_kernel<P, T>), dim3((unsigned)M), dim3(T), 0, s, staging, gamma, out, M, N, S, \
+                       eps, sys, status, lim)
     if (ppt <= 1)
-        hipLaunchKernelGGL(ar_rmsnorm_kernel<1>, dim3((unsigned)M), dim3(256), 0, s, staging, gamma, out, M, N, S,
-                           eps, sys, status, lim);
+        AREPI_RMS_LAUNCH(1, 256);
     else if (ppt <= 2)
-        hipLaunchKernelGGL(ar_rmsnorm_kernel<2>, dim3((unsigned)M), dim3(256), 0, s, staging, gamma, out, M, N, S,
-                           eps, sys, status, lim);
+        AREPI_RMS_LAUNCH(2, 256);
     else if (ppt <= 4)
-        hipLaunchKernelGGL(ar_rmsnorm_kernel<4>, dim3((unsigned)M), dim3(256), 0, s, staging, gamma, out, M, N, S,
-                           eps, sys, status, lim);
+        AREPI_RMS_LAUNCH(4, 256);
     else
-        hipLaunchKernelGGL(ar_rmsnorm_kernel<8>, dim3((unsigned)M), dim3(256), 0, s, staging, gamma, out, M, N, S,
-                           eps, sys, status, lim);
+        AREPI_RMS_LAUNCH(8, 256);
+#undef AREPI_RMS_LAUNCH
     return check_launch("arepi_ar_rmsnorm_lamport");
 }

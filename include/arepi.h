@@ -166,10 +166,20 @@ int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma, uint16_t 
  * stages are issued and waited on independently):
  *   out[t,h] = bf16( sum_{k<E} gate[t,k] * x[t,k,h] )    (fp32 accumulate)
  *   x bf16 [T,E,H], gate fp32 [T,E], out bf16 [T,H].
- * Constraints: 1 <= E <= 16, H % 8 == 0.
+ * Constraints: 1 <= E <= 16, H % 8 == 0.  This entry point streams the
+ * expert rows through registers (two work units in flight per thread,
+ * nontemporal loads and stores).
  * ------------------------------------------------------------------------ */
 int arepi_combine_reduce(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int E,
                          int64_t H, arepi_stream_t stream);
+
+/* The same combine through the LDS-staged pipeline: each wave owns S stages of
+ * E x 1 KiB filled by direct-to-LDS loads and waits for one stage at a time
+ * (the stage-per-issuer structure of the DeepEP fix above).  Same arguments,
+ * constraints and results as arepi_combine_reduce (identical bits: both add
+ * the experts in ascending order with the same fused multiply-adds). */
+int arepi_combine_reduce_lds(const uint16_t *x, const float *gate, uint16_t *out, int64_t T, int E,
+                             int64_t H, arepi_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * Test-only peer emulation on one GPU (prefixed emu_ so it is never mistaken

@@ -138,6 +138,8 @@ def test_lamport_and_combine_validate_before_launch():
     assert L.arepi_lamport_prefill(None, 0, None) == A.OK
     assert L.arepi_combine_reduce(None, None, None, 4, 17, 64, None) == A.EUNSUPPORTED
     assert "E=17" in A.last_error()
+    assert L.arepi_combine_reduce_lds(None, None, None, 4, 17, 64, None) == A.EUNSUPPORTED
+    assert L.arepi_combine_reduce_lds(None, None, None, 4, 8, 64, None) == A.EINVAL
     assert L.arepi_combine_reduce(None, None, None, 4, 8, 60, None) == A.EINVAL
     assert L.arepi_combine_reduce(None, None, None, 0, 8, 64, None) == A.OK  # empty: nothing to do
     assert L.arepi_combine_reduce(None, None, None, 4, 8, 64, None) == A.EINVAL
