@@ -7,7 +7,7 @@ in the library's HIP kernels; there is no fallback of any kind, and every call
 raises if ``libarepi.so`` is missing or a kernel launch is refused.
 
 Names mirror the C entry points without the ``arepi_`` prefix:
-  gemm_rs_fused, gemm_rs_supports, gemm_rs_flag_words, gemm_rs_pick_tile,
+  gemm_rs_fused, gemm_rs_supports, gemm_rs_flag_words, gemm_rs_pick_tile, gemm_rs_schedule,
   lamport_prefill, lamport_publish, ar_rmsnorm_lamport, combine_reduce (and its
   LDS-staged variant via pipeline="lds"),
   emu_peer_producer, last_error, version.
@@ -26,6 +26,7 @@ SCOPE_AGENT, SCOPE_SYSTEM = 0, 1
 STATUS_TIMEOUT = 1
 (TILE_AUTO, TILE_256x256, TILE_128x256, TILE_128x128, TILE_64x128, TILE_32x256, TILE_256x256_S4,
  TILE_256x128_S3, TILE_128x256_S3, TILE_128x128_S4) = range(10)
+TILE_CONTIGUOUS_ROWS = 0x100  # OR into an explicit tile: one contiguous row block per workgroup
 TILE_NAMES = {TILE_256x256: "256x256", TILE_128x256: "128x256", TILE_128x128: "128x128",
               TILE_64x128: "64x128", TILE_32x256: "32x256", TILE_256x256_S4: "256x256_s4",
               TILE_256x128_S3: "256x128_s3", TILE_128x256_S3: "128x256_s3", TILE_128x128_S4: "128x128_s4"}
@@ -62,6 +63,7 @@ def lib():
             "arepi_gemm_rs_supports": ([i64, i64, i64, i32, i32, i32, i32, i32, i32], i32),
             "arepi_gemm_rs_flag_words": ([i64, i64, i32, i32, i32], i64),
             "arepi_gemm_rs_pick_tile": ([i64, i64, i64, i32, i32, i32, i32, i32], i32),
+            "arepi_gemm_rs_schedule": ([i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, i64], i64),
             "arepi_gemm_rs_fused": ([vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
                                      u32p, i64, vp], i32),
             "arepi_lamport_prefill": ([vp, i64, vp], i32),
@@ -143,6 +145,17 @@ def gemm_rs_flag_words(M: int, N: int, R: int, flag_tile_m: int = 128, flag_tile
 def gemm_rs_supports(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publish=False, tile=TILE_AUTO) -> int:
     """0 when supported, else the negative status (message in last_error())."""
     return lib().arepi_gemm_rs_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish), tile)
+
+
+def gemm_rs_schedule(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publish=False, tile=TILE_AUTO):
+    """Work assignment of gemm_rs_fused: list of (row block, column block, a0, a_rows, b0, b_rows)
+    per workgroup in launch order (the rows it computes are [a0, a0+a_rows) and [b0, b0+b_rows))."""
+    n = _check(lib().arepi_gemm_rs_schedule(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish), tile,
+                                             None, 0), "gemm_rs_schedule")
+    buf = (ctypes.c_int64 * (6 * n))()
+    _check(lib().arepi_gemm_rs_schedule(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish), tile,
+                                        ctypes.cast(buf, ctypes.c_void_p), 6 * n), "gemm_rs_schedule")
+    return [tuple(buf[6 * i:6 * i + 6]) for i in range(n)]
 
 
 def gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publish=False) -> int:

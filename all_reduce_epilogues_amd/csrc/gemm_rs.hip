@@ -63,6 +63,13 @@ struct GemmRsParams {
     int R, owner, ftm, ftn;
     int system_scope;
     int nRB, nCB, ob1, group, xcd_chunk, nWG;
+    // Row blocks are two chunks of CK rows (A, B).  Contiguous: block b is rows
+    // [b*BM, (b+1)*BM).  Paired (seg a multiple of CK, R >= 2): chunks never
+    // straddle a segment; the first npure blocks pair two non-owner chunks, the
+    // next nleft (0/1) hold one non-owner chunk, the last nc pair owner chunk i
+    // with a non-owner chunk, so the owner rows' peer reads are spread over nc
+    // row blocks instead of seg/BM.
+    int paired, nc, npure, nleft;
 };
 
 // gfx9 buffer-resource word 3 (raw, untyped 32-bit data format).
@@ -113,7 +120,42 @@ __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_base, uint32_t vo
                  : "memory", "m0");
 }
 
-__device__ __forceinline__ void tile_of_block(const GemmRsParams &p, int b, int &rb, int &cb) {
+// Rows of a chunk that starts at `first` and holds at most CK rows.
+__host__ __device__ __forceinline__ int rows_left(int64_t M, int64_t first, int CK) {
+    const int64_t n = M - first;
+    return n <= 0 ? 0 : n < CK ? (int)n : CK;
+}
+
+// Global first row and row count of the two chunks of row block rb (shared by
+// the kernel and the host-side schedule query).
+__host__ __device__ __forceinline__ void chunks_of_block(const GemmRsParams &p, int BM, int CK, int rb, int64_t &a0,
+                                                         int &alen, int64_t &b0, int &blen) {
+    if (!p.paired) {
+        a0 = (int64_t)rb * BM;
+        b0 = a0 + CK;
+        alen = rows_left(p.M, a0, CK);
+        blen = CK < BM ? rows_left(p.M, b0, CK) : 0;
+        return;
+    }
+    // non-owner chunk j: segment owner+1+j/nc (mod R), chunk j%nc of it
+    auto other = [&](int j) { return (int64_t)((p.owner + 1 + j / p.nc) % p.R) * p.seg + (int64_t)(j % p.nc) * CK; };
+    const int tail = (p.R - 2) * p.nc;  // non-owner chunks before the ones paired with owner chunks
+    alen = blen = CK;
+    if (rb < p.npure) {
+        a0 = other(2 * rb);
+        b0 = other(2 * rb + 1);
+    } else if (rb < p.npure + p.nleft) {
+        a0 = other(tail - 1);
+        b0 = 0;
+        blen = 0;
+    } else {
+        const int i = rb - p.npure - p.nleft;
+        a0 = (int64_t)p.owner * p.seg + (int64_t)i * CK;
+        b0 = other(tail + i);
+    }
+}
+
+__host__ __device__ __forceinline__ void tile_of_block(const GemmRsParams &p, int b, int &rb, int &cb) {
     // XCD-aware remap inside full rounds of 8*C blocks: consecutive schedule
     // entries land on the same XCD (blocks are dealt to XCDs round-robin).
     const int C = p.xcd_chunk;
@@ -126,18 +168,24 @@ __device__ __forceinline__ void tile_of_block(const GemmRsParams &p, int b, int 
     // G row blocks at a time, column-major inside the group.
     const int per_group = p.group * p.nCB;
     const int g = s / per_group, within = s % per_group;
-    const int gsz = min(p.group, p.nRB - g * p.group);
+    const int gsz = p.group < p.nRB - g * p.group ? p.group : p.nRB - g * p.group;
     const int pos = g * p.group + within % gsz;
     cb = within / gsz;
     rb = (p.ob1 + pos) % p.nRB;  // rotated: owner row blocks come last
 }
 
-// WPE: waves per SIMD the register allocation targets (1 = one big-tile
-// workgroup per CU; 2 = two co-resident workgroups; 0 = no target).
-template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-    __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, WPE > 0 ? WPE : 8)))
-    gemm_rs_kernel(const GemmRsParams p) {
+// LDS bytes of one workgroup: S stages of [X tile | W tile].
+template <int BM, int BN, int BK, int S>
+constexpr int lds_bytes() { return S * (BM * BK * 2 + BK * BN * 2); }
+
+// Kinds of workgroup, fixed at entry so that each body has straight-line code
+// around the accumulators (a conditional update of them makes the compiler copy
+// all of them through vector registers).
+enum { kNoOwnerRows = 0, kOwnerChunkA = 1, kOwnerRowsAnywhere = 2 };
+
+template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, int KIND>
+__device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *smem, int rb, int cb, int64_t a0,
+                                             int alen, int64_t b0, int blen) {
     constexpr int NWN = BN / WN;
     constexpr int NW = (BM / WM) * NWN;
     constexpr int TM = WM / 32, TN = WN / 32;
@@ -161,16 +209,26 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     static_assert(NW * ER * EPS * 4 <= LDS_BYTES, "epilogue slabs must fit the stage memory");
     static_assert(S >= 2 && (S - 2) * NDMA < 64, "stage count vs vmcnt range");
 
-    // S stages [X | W] x S; the epilogue reuses the same memory.
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+    static_assert(LDS_BYTES == lds_bytes<BM, BN, BK, S>(), "stage layout");
+    // S stages [X | W] x S (in `smem`); the epilogue reuses the same memory.
     typedef __attribute__((address_space(3))) uint8_t lds_t;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / NWN, wn = wave % NWN;
-    int rb, cb;
-    tile_of_block(p, blockIdx.x, rb, cb);
-    const int64_t m0 = (int64_t)rb * BM, n0 = (int64_t)cb * BN;
+    (void)rb;
+    const int64_t n0 = (int64_t)cb * BN;
     const int64_t M = p.M, N = p.N, K = p.K;
+    // The tile's BM rows are two chunks A and B of CK rows, interleaved in
+    // blocks of IL rows so that every wave row holds as many rows of A as of B
+    // (an owner chunk's epilogue work is shared by all waves).
+    constexpr int IL = BM >= 64 ? (WM >= 64 ? WM / 2 : WM) : BM;
+    constexpr int CK = BM >= 64 ? BM / 2 : BM;
+    static_assert(BM < 64 || (BM / (2 * IL)) * IL == CK, "chunk interleave");
+    // global row of tile row v, or -1 past the end of its chunk
+    auto row_of = [&](int v) -> int64_t {
+        const int idx = (v / (2 * IL)) * IL + v % IL;
+        return ((v / IL) & 1) ? (idx < blen ? b0 + idx : -1) : (idx < alen ? a0 + idx : -1);
+    };
 
     // Buffer resources over X and W: a load whose offset is out of range
     // returns zeros, which fills the M, N and K tails without branches.
@@ -190,8 +248,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     uint32_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
-        const int64_t gm = m0 + a_row_of(i);
-        a_off[i] = (gm < M) ? (uint32_t)((gm * K + a_col_of(i)) * 2) : kOob;
+        const int64_t gm = row_of(a_row_of(i));
+        a_off[i] = (gm >= 0) ? (uint32_t)((gm * K + a_col_of(i)) * 2) : kOob;
     }
 #pragma unroll
     for (int i = 0; i < B_INSTR; ++i) {
@@ -333,33 +391,55 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     float *const ep = reinterpret_cast<float *>(smem) + wave * ER * EPS;
 
     // ---- epilogue -----------------------------------------------------------------
+    // Row and byte offsets are 32-bit: M*N*2, M*K*2 and K*N*2 are below 2 GiB.
     const bool sys = p.system_scope != 0;
-    const int64_t m1 = min(m0 + BM, M);
-    const int64_t oseg0 = (int64_t)p.owner * p.seg, oseg1 = oseg0 + p.seg;
-    const bool has_owner = m0 < oseg1 && m1 > oseg0;
-    const bool has_other = m0 < oseg0 || m1 > oseg1;
+    const int seg = (int)p.seg, Ni = (int)N, N2 = 2 * (int)N;
+    const int oseg0 = p.owner * seg, oseg1 = oseg0 + seg;
+    // the tile's rows as up to two ranges [r0[h], r1[h]) (one when B follows
+    // A; empty ranges have r0 == r1); loops over h are unrolled so that these
+    // stay in registers
+    int r0[2], r1[2];
+    if (alen > 0 && blen > 0 && (int)b0 == (int)a0 + alen) {
+        r0[0] = (int)a0, r1[0] = (int)a0 + alen + blen, r0[1] = r1[1] = 0;
+    } else {
+        r0[0] = (int)a0, r1[0] = (int)a0 + max(alen, 0);
+        r0[1] = (int)b0, r1[1] = (int)b0 + max(blen, 0);
+    }
+    constexpr bool has_owner = KIND != kNoOwnerRows;
+    bool has_other = false;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) has_other |= r0[h] < r1[h] && (r0[h] < oseg0 || r1[h] > oseg1);
+    const int tc0 = (int)(n0 / p.ftn), ntc = (int)((min(n0 + BN, N) - 1) / p.ftn) - tc0 + 1;
 
-    if (has_owner) {
-        // Wait until every peer's flag tiles under this tile's owner rows are set.
-        if (wave == 0 && lane < p.R && lane != p.owner) {
-            const int64_t lr0 = max(m0, oseg0) - oseg0, lr1 = min(m1, oseg1) - oseg0;
-            const int64_t tr0 = lr0 / p.ftm, tr1 = (lr1 - 1) / p.ftm;
-            const int64_t tc0 = n0 / p.ftn, tc1 = (min(n0 + BN, N) - 1) / p.ftn;
-            const uint32_t *words = p.ready_in + (int64_t)lane * p.fwords;
+    if constexpr (has_owner) {
+        // Wait until every peer's flag tiles under this tile's owner rows are
+        // set: one (peer, flag tile) item per lane, all polled at once with
+        // relaxed loads, then one acquire.
+        if (wave == 0) {
+            int tr0[2] = {0, 0}, th[2] = {0, 0};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (!(r0[h] < r1[h] && r0[h] < oseg1 && r1[h] > oseg0)) continue;
+                const int lr0 = max(r0[h], oseg0) - oseg0, lr1 = min(r1[h], oseg1) - oseg0;
+                tr0[h] = lr0 / p.ftm;
+                th[h] = ((lr1 - 1) / p.ftm - tr0[h] + 1) * ntc;
+            }
+            const int per_peer = th[0] + th[1], items = p.npeers * per_peer;
             int64_t spins = 0;
-            bool gave_up = false;
-            for (int64_t tr = tr0; tr <= tr1 && !gave_up; ++tr) {
-                for (int64_t tc = tc0; tc <= tc1 && !gave_up; ++tc) {
-                    const int64_t t = tr * p.ftiles_n + tc;
-                    const uint32_t bit = 1u << (t & 31);
-                    while (!(load_relaxed(words + (t >> 5), sys) & bit)) {
-                        if (++spins > p.spin_limit) {
-                            if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
-                            gave_up = true;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(2);
+            for (int k = lane; k < items; k += 64) {
+                const int slot = k / per_peer;
+                int ti = k % per_peer;
+                const int h = ti < th[0] ? 0 : 1;
+                ti -= h ? th[0] : 0;
+                const int t = ((h ? tr0[1] : tr0[0]) + ti / ntc) * (int)p.ftiles_n + tc0 + ti % ntc;
+                const int rank = slot < p.owner ? slot : slot + 1;
+                const uint32_t *word = p.ready_in + (int64_t)rank * p.fwords + (t >> 5);
+                while (!(load_relaxed(word, sys) & (1u << (t & 31)))) {
+                    if (++spins > p.spin_limit) {
+                        if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
+                        break;
                     }
+                    __builtin_amdgcn_s_sleep(2);
                 }
             }
             fence_acquire(sys);
@@ -367,90 +447,184 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
         __syncthreads();
     }
 
+    // Peer combine on the matrix cores.  For every 32-row accumulator block
+    // holding owner rows, each peer's partial P (bf16, ascending rank order) is
+    // added as acc += P[:, 0:16] x I[0:16, :] + P[:, 16:32] x I[16:32, :]: each
+    // output element receives exactly one nonzero product p x 1.0 (exact), so
+    // the result is the fp32 sum acc + p rounded once, peer after peer, as a
+    // vector add would give it.  P is loaded straight into the MFMA A-operand
+    // layout (lane l: row l%32, 8 consecutive columns); rows that are not owner
+    // rows, columns past N and slots past R-1 load zeros (out-of-range buffer
+    // offsets), adding +0.0.
+    const int wm_u = wave_u / NWN;
+    // Chunk (hb: false = A, true = B) and row inside it of this wave's row
+    // wm*WM + t (t < WM, a multiple of 8).  When WM is a multiple of 2*IL the
+    // chunk depends on t alone, which keeps it a compile-time constant.
+    constexpr bool kStaticHalves = WM % (2 * IL) == 0;
+    auto chunk_pos = [&](int t, bool &hb, int &idx) {
+        if constexpr (kStaticHalves) {
+            hb = (t / IL) & 1;
+            idx = wm_u * (WM / 2) + (t / (2 * IL)) * IL + t % IL;
+        } else {
+            const unsigned v = (unsigned)(wm_u * WM + t);
+            hb = (v / IL) & 1;
+            idx = (int)((v / (2 * IL)) * IL + v % IL);
+        }
+    };
+
+    // ---- staging, peer combine and stores ---------------------------------------
     // Each wave drains its accumulators one ER-row slab at a time through its
     // own LDS region (no workgroup barrier: a wave's LDS operations complete in
-    // order) and finishes row-contiguous 16-byte packs.  The peers' partials of
-    // owner rows are independent of the accumulators, so they are fetched D
-    // units ahead (a unit = one 16-byte pack per lane) with branch-free buffer
-    // loads; out-of-range and non-owner lanes use an out-of-range offset.
+    // order) and finishes row-contiguous 16-byte packs ("units": one pack per
+    // lane, RPS rows x WN columns per wave).  All LDS reads of a slab are
+    // issued before its packs are used.  Row bases of a unit are wave-uniform
+    // scalars; each lane adds a fixed byte offset.
+    //  * Owner rows add the peers' partials (bf16 -> fp32, ascending rank
+    //    order) to the fp32 accumulator, then round once.  The peers' packs
+    //    are fetched D units ahead with row-coalesced buffer loads; lanes whose
+    //    row is not an owner row and slots past R-1 use an out-of-range offset
+    //    (the load returns zeros) and have their bits ORed with 0x80008000, so
+    //    they add -0.0, which leaves every value unchanged.
+    //  * A pack is stored with buffer stores whose offset is out of range
+    //    (nothing is written) for the destination its row does not belong to
+    //    and for rows or columns past the end.
+    //  * When the owner chunk is A and the halves are static, the B half-blocks
+    //    (no owner rows) are drained first, while the first peer packs load.
     constexpr int CPR = WN / 8;     // 16-byte chunks per epilogue row
     constexpr int RPS = 64 / CPR;   // rows per unit
     constexpr int STEPS = ER / RPS; // units per slab
     constexpr int NQ = 32 / ER;     // slabs per 32-row MFMA block
-    constexpr int NU = TM * NQ * STEPS;
-    constexpr int kPeers = PEERS;       // peer slots compiled in (>= R - 1)
-    constexpr int DW = WPE != 1 ? (PEERS <= 3 ? 4 : 2) : (PEERS <= 3 ? 8 : 4);
-    constexpr int D = NU < DW ? NU : DW;  // prefetch depth in units
+    constexpr int UPB = NQ * STEPS; // units per 32-row block
     static_assert(STEPS >= 1 && STEPS * RPS == ER, "epilogue step split");
-    const uint32_t recv_bytes = (uint32_t)(p.seg * N * 2);
-    __amdgpu_buffer_rsrc_t prs[kPeers];
-    bool pvalid[kPeers];
-#pragma unroll
-    for (int sl = 0; sl < kPeers; ++sl) {  // slots hold the peers in ascending rank order
-        pvalid[sl] = sl < p.npeers;
-        prs[sl] = __builtin_amdgcn_make_buffer_rsrc((void *)(pvalid[sl] ? p.peer[sl] : p.x), 0,
-                                                    pvalid[sl] ? (int)recv_bytes : 0, kBufferDword3);
-    }
-    auto unit_pos = [&](int u, int64_t &gr, int64_t &gc, int &row, int &ch) {
-        const int i = u / (NQ * STEPS), q = (u / STEPS) % NQ, st = u % STEPS;
-        row = st * RPS + lane / CPR;
-        ch = lane % CPR;
-        gr = m0 + wm * WM + i * 32 + q * ER + row;
-        gc = n0 + wn * WN + ch * 8;
+    constexpr bool kAOnly = KIND == kOwnerChunkA && kStaticHalves;
+    auto block_is_a = [](int i) { return !(((i * 32) / IL) & 1); };
+    // owner-candidate blocks, in drain order
+    constexpr int NOB = KIND == kNoOwnerRows ? 0 : kAOnly ? (TM + 1) / 2 : TM;
+    auto cand_block = [&](int c) {
+        if constexpr (kAOnly) {
+            int n = 0;
+            for (int i = 0; i < TM; ++i)
+                if (block_is_a(i) && n++ == c) return i;
+            return 0;
+        } else {
+            return c;
+        }
     };
-    auto prefetch = [&](int u, i32x4 (&pk)[kPeers]) {
-        int64_t gr, gc;
-        int row, ch;
-        unit_pos(u, gr, gc, row, ch);
-        const bool own = gr >= oseg0 && gr < oseg1 && gc < N;
-        const uint32_t off = own ? (uint32_t)(((gr - oseg0) * N + gc) * 2) : kOob;
-#pragma unroll
-        for (int sl = 0; sl < kPeers; ++sl)
-            if (pvalid[sl])
-                pk[sl] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(prs[sl], off, 0, kAuxNontemporal));
+    constexpr int NOU = NOB * UPB;  // owner-candidate units
+    constexpr int DW = (WPE != 1 ? 1 : 2) * (PEERS <= 1 ? 8 : PEERS <= 3 ? 4 : 2);
+    constexpr int D = NOU < DW ? NOU : DW;  // prefetch depth in units
+    const int lane_r = lane / CPR, ch = lane % CPR;
+    const int gc = (int)n0 + wn * WN + ch * 8;
+    const bool col_ok = gc < Ni;
+    const int lane_off = lane_r * N2 + gc * 2;  // byte offset of this lane inside a unit
+    const __amdgpu_buffer_rsrc_t out_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.out, 0, seg * N2, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t send_rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(p.send ? p.send : p.out), 0, p.send ? (int)(M * N2) : 0, kBufferDword3);
+    // Unit (block i, slab q, step st): first global row (scalar) and how many of its RPS rows exist.
+    auto unit_rows = [&](int i, int q, int st, int &row0, int &nrows) {
+        bool hb;
+        int idx;
+        chunk_pos(i * 32 + q * ER + st * RPS, hb, idx);
+        row0 = (hb ? (int)b0 : (int)a0) + idx;
+        nrows = min(max((hb ? blen : alen) - idx, 0), RPS);
     };
-    i32x4 pk[D][kPeers];
-    if (has_owner) {
+    // byte offset of this lane's pack of a unit in the owner segment, or out of range
+    auto owner_off = [&](int row0, int nrows) -> uint32_t {
+        const int row = row0 + lane_r;
+        const bool own = col_ok && lane_r < nrows && row >= oseg0 && row < oseg1;
+        return own ? (uint32_t)((row0 - oseg0) * N2 + lane_off) : kOob;
+    };
+    __amdgpu_buffer_rsrc_t prs[PEERS];
+    uint32_t pneg[PEERS];  // 0x80008000 for slots past R-1 (they add -0.0)
+    i32x4 pk[D > 0 ? D : 1][PEERS];
+    auto prefetch = [&](int ou) {  // ou = owner-candidate unit
+        const int i = cand_block(ou / UPB), q = (ou % UPB) / STEPS, st = ou % STEPS;
+        int row0, nrows;
+        unit_rows(i, q, st, row0, nrows);
+        const uint32_t off = owner_off(row0, nrows);
 #pragma unroll
-        for (int u = 0; u < D; ++u) prefetch(u, pk[u]);
+        for (int sl = 0; sl < PEERS; ++sl)
+            pk[ou % D][sl] =
+                __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(prs[sl], off, 0, kAuxNontemporal));
+    };
+    if constexpr (NOU > 0) {
+        const int recv_bytes = seg * N2;
+#pragma unroll
+        for (int sl = 0; sl < PEERS; ++sl) {  // slots hold the peers in ascending rank order
+            const bool valid = sl < p.npeers;
+            prs[sl] = __builtin_amdgcn_make_buffer_rsrc((void *)(valid ? p.peer[sl] : p.x), 0,
+                                                        valid ? recv_bytes : 0, kBufferDword3);
+            pneg[sl] = valid ? 0u : 0x80008000u;
+        }
+#pragma unroll
+        for (int ou = 0; ou < D; ++ou) prefetch(ou);
     }
+    // Drain block i; `c` is its index among the owner-candidate blocks, or -1.
+    auto drain_block = [&](int i, int c) {
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const int i = u / (NQ * STEPS), q = (u / STEPS) % NQ;
-        if (u % STEPS == 0) {
+        for (int q = 0; q < NQ; ++q) {
             // accumulator register r of a 32x32 tile holds row 8*(r/4) + 4*(lane/32) + r%4
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    if (row / ER == q) ep[(row % ER) * EPS + j * 32 + (lane & 31)] = acc[i][j][r];
+                    if (NQ == 1 || row / ER == q) ep[(row % ER) * EPS + j * 32 + (lane & 31)] = acc[i][j][r];
                 }
-        }
-        int64_t gr, gc;
-        int row, ch;
-        unit_pos(u, gr, gc, row, ch);
-        if (gr < M && gc < N) {
-            const float4 v0 = *reinterpret_cast<const float4 *>(ep + row * EPS + ch * 8);
-            const float4 v1 = *reinterpret_cast<const float4 *>(ep + row * EPS + ch * 8 + 4);
-            float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            if (gr >= oseg0 && gr < oseg1) {
+            float v[STEPS][8];
 #pragma unroll
-                for (int sl = 0; sl < kPeers; ++sl) {
-                    if (pvalid[sl]) {
+            for (int st = 0; st < STEPS; ++st) {
+                const float *src = ep + (st * RPS + lane_r) * EPS + ch * 8;
+                const float4 v0 = *reinterpret_cast<const float4 *>(src);
+                const float4 v1 = *reinterpret_cast<const float4 *>(src + 4);
+                v[st][0] = v0.x, v[st][1] = v0.y, v[st][2] = v0.z, v[st][3] = v0.w;
+                v[st][4] = v1.x, v[st][5] = v1.y, v[st][6] = v1.z, v[st][7] = v1.w;
+            }
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st) {
+                int row0, nrows;
+                unit_rows(i, q, st, row0, nrows);
+                const int row = row0 + lane_r;
+                const bool ok = col_ok && lane_r < nrows;
+                const bool own = row >= oseg0 && row < oseg1;
+                if (c >= 0) {  // compile-time after unrolling
+                    const int ou = c * UPB + q * STEPS + st;
+                    const uint32_t lane_neg = owner_off(row0, nrows) == kOob ? 0x80008000u : 0u;
+#pragma unroll
+                    for (int sl = 0; sl < PEERS; ++sl) {
+                        const uint32_t neg = lane_neg | pneg[sl];
+                        const i32x4 w4 = pk[ou % D][sl];
                         float f[8];
-                        const i32x4 w4 = pk[u % D][sl];
-                        unpack8(make_uint4(w4.x, w4.y, w4.z, w4.w), f);
+                        unpack8(make_uint4((uint32_t)w4.x | neg, (uint32_t)w4.y | neg, (uint32_t)w4.z | neg,
+                                           (uint32_t)w4.w | neg),
+                                f);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] = v[e] + f[e];
+                        for (int e = 0; e < 8; ++e) v[st][e] = v[st][e] + f[e];
                     }
+                    if (ou + D < NOU) prefetch(ou + D);
                 }
-                store16_nt(p.out + (gr - oseg0) * N + gc, pack8(v));
-            } else if (p.send) {
-                store16_nt(p.send + gr * N + gc, pack8(v));
+                const uint4 q8 = pack8(v[st]);
+                const i32x4 qv = {(int)q8.x, (int)q8.y, (int)q8.z, (int)q8.w};
+                if constexpr (has_owner)
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        qv, out_rs, (ok && own) ? (uint32_t)((row0 - oseg0) * N2 + lane_off) : kOob, 0,
+                        kAuxNontemporal);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    qv, send_rs, (ok && !own) ? (uint32_t)(row0 * N2 + lane_off) : kOob, 0, kAuxNontemporal);
             }
         }
-        if (has_owner && u + D < NU) prefetch(u + D, pk[u % D]);
+    };
+
+    if constexpr (kAOnly) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            if (!block_is_a(i)) drain_block(i, -1);
+#pragma unroll
+        for (int c = 0; c < NOB; ++c) drain_block(cand_block(c), c);
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) drain_block(i, KIND == kNoOwnerRows ? -1 : i);
     }
 
     // Publish the send tiles: drain this thread's stores, balanced barrier, one
@@ -460,23 +634,49 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
         __syncthreads();
         if (wave == 0) {
             fence_release(sys);
-            const int64_t d0 = m0 / p.seg, d1 = (m1 - 1) / p.seg;
-            const int64_t tc0 = n0 / p.ftn, tc1 = (min(n0 + BN, N) - 1) / p.ftn;
-            const int64_t ntc = tc1 - tc0 + 1;
-            for (int64_t d = d0; d <= d1; ++d) {
-                if (d == p.owner) continue;
-                const int64_t s0 = d * p.seg;
-                const int64_t lr0 = max(m0, s0) - s0, lr1 = min(m1, s0 + p.seg) - s0;
-                const int64_t tr0 = lr0 / p.ftm, tr1 = (lr1 - 1) / p.ftm;
-                const int64_t items = (tr1 - tr0 + 1) * ntc;
-                uint32_t *words = p.ready_out + d * p.fwords;
-                for (int64_t it = lane; it < items; it += 64) {
-                    const int64_t t = (tr0 + it / ntc) * p.ftiles_n + tc0 + it % ntc;
-                    fetch_or_relaxed(words + (t >> 5), 1u << (t & 31), sys);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (r0[h] >= r1[h]) continue;
+                const int d0 = r0[h] / seg, d1 = (r1[h] - 1) / seg;
+                for (int d = d0; d <= d1; ++d) {
+                    if (d == p.owner) continue;
+                    const int s0 = d * seg;
+                    const int lr0 = max(r0[h], s0) - s0, lr1 = min(r1[h], s0 + seg) - s0;
+                    const int tr0 = lr0 / p.ftm, tr1 = (lr1 - 1) / p.ftm;
+                    const int items = (tr1 - tr0 + 1) * ntc;
+                    uint32_t *words = p.ready_out + (int64_t)d * p.fwords;
+                    for (int it = lane; it < items; it += 64) {
+                        const int t = (tr0 + it / ntc) * (int)p.ftiles_n + tc0 + it % ntc;
+                        fetch_or_relaxed(words + (t >> 5), 1u << (t & 31), sys);
+                    }
                 }
             }
         }
     }
+}
+
+// WPE: waves per SIMD the register allocation targets (1 = one big-tile
+// workgroup per CU; 2 = two co-resident workgroups; 0 = no target).
+template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+    __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, WPE > 0 ? WPE : 8)))
+    gemm_rs_kernel(const GemmRsParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<BM, BN, BK, S>()];
+    constexpr int CK = BM >= 64 ? BM / 2 : BM;
+    int rb, cb;
+    tile_of_block(p, blockIdx.x, rb, cb);
+    int64_t a0, b0;
+    int alen, blen;
+    chunks_of_block(p, BM, CK, rb, a0, alen, b0, blen);
+    const int64_t oseg0 = (int64_t)p.owner * p.seg, oseg1 = oseg0 + p.seg;
+    const bool own_a = alen > 0 && a0 < oseg1 && a0 + alen > oseg0;
+    const bool own_b = blen > 0 && b0 < oseg1 && b0 + blen > oseg0;
+    if (!own_a && !own_b)
+        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kNoOwnerRows>(p, smem, rb, cb, a0, alen, b0, blen);
+    else if (p.paired)  // paired half-blocks: only chunk A can be an owner chunk
+        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerChunkA>(p, smem, rb, cb, a0, alen, b0, blen);
+    else
+        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerRowsAnywhere>(p, smem, rb, cb, a0, alen, b0, blen);
 }
 
 // ---- host side --------------------------------------------------------------------
@@ -508,8 +708,9 @@ const TileCfg *find_tile(int id) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Every flag tile (of every segment) must lie inside one compute tile, so that
-// one workgroup can publish it.
+// Every flag tile (of every segment) must lie inside one row block of BM rows
+// (or chunk, in the paired layout: the same test with BM = CK) and one column
+// block of BN, so that one workgroup can publish it.
 bool flags_nest(int64_t M, int64_t N, int R, int ftm, int ftn, int BM, int BN) {
     const int64_t seg = M / R;
     for (int64_t c = 0; c * ftn < N; ++c) {
@@ -538,9 +739,21 @@ int validate_shape(int64_t M, int64_t N, int64_t K, int R, int owner, int ftm, i
         return bad("flag tile " + std::to_string(ftm) + "x" + std::to_string(ftn) + " must be at least 1x1");
     // X, W and each peer partial are addressed with 32-bit buffer offsets
     const int64_t lim = int64_t(1) << 31;
-    if (M * K * 2 >= lim || K * N * 2 >= lim || (M / R) * N * 2 >= lim)
-        return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: X, W and each peer partial must be below 2 GiB");
+    if (M * K * 2 >= lim || K * N * 2 >= lim || M * N * 2 >= lim)
+        return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: X [M,K], W [K,N] and send [M,N] must each be below 2 GiB");
     return AREPI_OK;
+}
+
+// Chunk rows of a BM-row block (two chunks per block from BM = 64 up).
+int chunk_rows(int BM) { return BM >= 64 ? BM / 2 : BM; }
+
+// Whether the paired row layout applies: two or more ranks, segments made of
+// whole chunks, and (when publishing) flag tiles nested in chunks.
+bool use_paired(int64_t M, int64_t N, int R, int ftm, int ftn, int BM, int BN, bool publish, bool contiguous) {
+    const int CK = chunk_rows(BM);
+    if (contiguous || R < 2 || CK == BM) return false;
+    if ((M / R) % CK) return false;
+    return !publish || flags_nest(M, N, R, ftm, ftn, CK, BN);
 }
 
 int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool publish) {
@@ -548,7 +761,9 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool pub
     int best = -1;
     double best_cost = 0;
     for (const auto &t : kTiles) {
-        if (publish && !flags_nest(M, N, R, ftm, ftn, t.BM, t.BN)) continue;
+        if (publish && !flags_nest(M, N, R, ftm, ftn, t.BM, t.BN) &&
+            !use_paired(M, N, R, ftm, ftn, t.BM, t.BN, true, false))
+            continue;
         const int64_t count = cdiv(M, t.BM) * cdiv(N, t.BN);
         // waves of co-resident tiles x work per CU per wave / efficiency
         const double cost = (double)cdiv(count, 256 * t.slots) * t.slots * t.BM * t.BN / t.eff;
@@ -560,10 +775,48 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool pub
     return best;
 }
 
+// Launch geometry (everything but the pointers) for tile t.
+int plan(GemmRsParams &p, const TileCfg *t, int64_t M, int64_t N, int64_t K, int R, int owner, int ftm, int ftn,
+         bool publish, bool contiguous) {
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.seg = M / R;
+    p.ftiles_n = cdiv(N, ftn);
+    p.fwords = cdiv(cdiv(p.seg, ftm) * p.ftiles_n, 32);
+    p.R = R;
+    p.owner = owner;
+    p.ftm = ftm;
+    p.ftn = ftn;
+    p.nCB = (int)cdiv(N, t->BN);
+    p.paired = use_paired(M, N, R, ftm, ftn, t->BM, t->BN, publish, contiguous);
+    if (p.paired) {
+        // non-owner chunks paired with each other first, owner chunks paired last
+        const int CK = chunk_rows(t->BM);
+        p.nc = (int)(p.seg / CK);
+        p.npure = (R - 2) * p.nc / 2;
+        p.nleft = (R - 2) * p.nc % 2;
+        p.nRB = p.npure + p.nleft + p.nc;
+        p.ob1 = 0;
+    } else {
+        p.nRB = (int)cdiv(M, t->BM);
+        // first row block after the owner's: the rotation puts the owner's last
+        p.ob1 = (int)(cdiv((int64_t)(owner + 1) * p.seg, t->BM) % p.nRB);
+    }
+    p.group = 4;
+    p.xcd_chunk = 32;
+    const int64_t nwg = (int64_t)p.nRB * p.nCB;
+    if (nwg > (int64_t)1 << 30) return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: too many tiles");
+    p.nWG = (int)nwg;
+    return AREPI_OK;
+}
+
 template <int BM, int BN, int WM, int WN, int BK, int S, int WPE>
 void launch(const GemmRsParams &p, hipStream_t stream) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
-    if (p.npeers <= 3)
+    if (p.npeers <= 1)
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1>), dim3(p.nWG), dim3(NT), 0, stream, p);
+    else if (p.npeers <= 3)
         hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3>), dim3(p.nWG), dim3(NT), 0, stream, p);
     else
         hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1>), dim3(p.nWG), dim3(NT), 0,
@@ -605,9 +858,12 @@ extern "C" int arepi_gemm_rs_supports(int64_t M, int64_t N, int64_t K, int R, in
         rc = arepi_gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish);
         return rc < 0 ? rc : ok();
     }
-    const TileCfg *t = find_tile(tile_cfg);
+    const bool contiguous = (tile_cfg & AREPI_TILE_CONTIGUOUS_ROWS) != 0;
+    const int id = tile_cfg & ~AREPI_TILE_CONTIGUOUS_ROWS;
+    const TileCfg *t = id == AREPI_TILE_AUTO ? nullptr : find_tile(id);
     if (!t) return fail(AREPI_EINVAL, "arepi_gemm_rs: tile_cfg=" + std::to_string(tile_cfg) + " is not an AREPI_TILE_* value");
-    if (publish && !flags_nest(M, N, R, flag_tile_m, flag_tile_n, t->BM, t->BN))
+    if (publish && !flags_nest(M, N, R, flag_tile_m, flag_tile_n, t->BM, t->BN) &&
+        !use_paired(M, N, R, flag_tile_m, flag_tile_n, t->BM, t->BN, true, contiguous))
         return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: flag tiles " + std::to_string(flag_tile_m) + "x" +
                                             std::to_string(flag_tile_n) + " straddle " + std::to_string(t->BM) +
                                             "x" + std::to_string(t->BN) + " compute tiles");
@@ -638,7 +894,9 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
             if (!aligned16(recv[p])) return bad("recv[" + std::to_string(p) + "] must be 16-byte aligned");
         }
     }
-    const int cfg = tile_cfg == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, flag_tile_m, flag_tile_n, publish) : tile_cfg;
+    const bool contiguous = (tile_cfg & AREPI_TILE_CONTIGUOUS_ROWS) != 0;
+    const int cfg = tile_cfg == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, flag_tile_m, flag_tile_n, publish)
+                                                : tile_cfg & ~AREPI_TILE_CONTIGUOUS_ROWS;
     const TileCfg *t = find_tile(cfg);
 
     GemmRsParams p{};
@@ -652,27 +910,10 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
     p.send = send;
     p.ready_out = ready_out;
     p.status = status;
-    p.M = M;
-    p.N = N;
-    p.K = K;
-    p.seg = M / R;
-    p.ftiles_n = cdiv(N, flag_tile_n);
-    p.fwords = cdiv(cdiv(p.seg, flag_tile_m) * p.ftiles_n, 32);
     p.spin_limit = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
-    p.R = R;
-    p.owner = owner;
-    p.ftm = flag_tile_m;
-    p.ftn = flag_tile_n;
     p.system_scope = scope == AREPI_SCOPE_SYSTEM;
-    p.nRB = (int)cdiv(M, t->BM);
-    p.nCB = (int)cdiv(N, t->BN);
-    // first row block after the owner's: the rotation puts the owner's last
-    p.ob1 = (int)(cdiv((int64_t)(owner + 1) * p.seg, t->BM) % p.nRB);
-    p.group = 4;
-    p.xcd_chunk = 32;
-    const int64_t nwg = (int64_t)p.nRB * p.nCB;
-    if (nwg > (int64_t)1 << 30) return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_fused: too many tiles");
-    p.nWG = (int)nwg;
+    rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, publish, contiguous);
+    if (rc) return rc;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (cfg) {
@@ -688,4 +929,34 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
         default: return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_fused: no kernel for tile " + std::to_string(cfg));
     }
     return check_launch("arepi_gemm_rs_fused");
+}
+
+extern "C" int64_t arepi_gemm_rs_schedule(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
+                                          int flag_tile_n, int publish, int tile_cfg, int64_t *rows,
+                                          int64_t capacity) {
+    int rc = arepi_gemm_rs_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish, tile_cfg);
+    if (rc) return rc;
+    const bool contiguous = (tile_cfg & AREPI_TILE_CONTIGUOUS_ROWS) != 0;
+    const int cfg = tile_cfg == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, flag_tile_m, flag_tile_n, publish != 0)
+                                                : tile_cfg & ~AREPI_TILE_CONTIGUOUS_ROWS;
+    const TileCfg *t = find_tile(cfg);
+    GemmRsParams p{};
+    rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, publish != 0, contiguous);
+    if (rc) return rc;
+    if (rows) {
+        if (capacity < (int64_t)p.nWG * 6)
+            return fail(AREPI_EINVAL, "arepi_gemm_rs_schedule: capacity " + std::to_string(capacity) + " < 6 x " +
+                                          std::to_string(p.nWG) + " workgroups");
+        const int CK = chunk_rows(t->BM);
+        for (int b = 0; b < p.nWG; ++b) {
+            int rb, cb, alen, blen;
+            int64_t a0, b0;
+            tile_of_block(p, b, rb, cb);
+            chunks_of_block(p, t->BM, CK, rb, a0, alen, b0, blen);
+            int64_t *r = rows + (int64_t)b * 6;
+            r[0] = rb, r[1] = cb, r[2] = a0, r[3] = alen, r[4] = b0, r[5] = blen;
+        }
+    }
+    ok();
+    return p.nWG;
 }

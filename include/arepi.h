@@ -67,7 +67,13 @@ enum {
     AREPI_TILE_256x256_S4 = 6,
     AREPI_TILE_256x128_S3 = 7,
     AREPI_TILE_128x256_S3 = 8,
-    AREPI_TILE_128x128_S4 = 9
+    AREPI_TILE_128x128_S4 = 9,
+    /* ORed into an explicit tile: keep each workgroup's rows one contiguous
+     * block.  Otherwise, when every segment is a whole number of half-blocks,
+     * a workgroup takes two half-blocks (BM/2 rows each, BM >= 64) and the
+     * owner segment's half-blocks are each paired with a non-owner one, which
+     * spreads the owner rows' peer reads over twice as many workgroups. */
+    AREPI_TILE_CONTIGUOUS_ROWS = 0x100
 };
 
 /* Message describing the last failed call on this thread ("" if none). */
@@ -117,6 +123,16 @@ int64_t arepi_gemm_rs_flag_words(int64_t M, int64_t N, int R, int flag_tile_m, i
  * negative status. */
 int arepi_gemm_rs_pick_tile(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
                             int flag_tile_n, int publish);
+
+/* Work assignment of arepi_gemm_rs_fused for a shape (for tests and
+ * diagnostics): returns the number of workgroups W, or a negative status.  If
+ * rows is non-NULL (capacity >= 6*W int64 entries), workgroup b (in launch
+ * order) gets rows[6b..6b+5] = {row block, column block, first row of chunk A,
+ * rows of A, first row of chunk B, rows of B}; the workgroup computes the
+ * output rows of both chunks over columns [column block * BN, + BN). */
+int64_t arepi_gemm_rs_schedule(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
+                               int flag_tile_n, int publish, int tile_cfg, int64_t *rows,
+                               int64_t capacity);
 
 int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const uint16_t *const *recv,
                         const uint32_t *ready_in, uint16_t *out, uint16_t *send,

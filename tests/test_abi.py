@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import all_reduce_epilogues_amd as A
@@ -63,10 +64,65 @@ TILE_DIMS = A.TILE_DIMS
 ])
 def test_supports_matches_flag_nesting(M, N, R, ftm, ftn):
     for tile, (BM, BN) in TILE_DIMS.items():
-        rc = A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=True, tile=tile)
+        # contiguous row blocks: flag tiles must nest in BM x BN blocks
+        rc = A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=True, tile=tile | A.TILE_CONTIGUOUS_ROWS)
         assert (rc == 0) == nests(M, N, R, ftm, ftn, BM, BN), (tile, A.last_error())
+        # paired half-blocks are a second way to nest them
+        rc = A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=True, tile=tile)
+        expect = nests(M, N, R, ftm, ftn, BM, BN) or (paired_eligible(M, R, BM) and
+                                                      nests(M, N, R, ftm, ftn, BM // 2, BN))
+        assert (rc == 0) == expect, (tile, A.last_error())
         # without publication every tile is allowed
         assert A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=False, tile=tile) == 0
+
+
+def paired_eligible(M, R, BM):
+    """Half-blocks of BM/2 rows can be paired when every segment is made of whole half-blocks."""
+    return R >= 2 and BM >= 64 and (M // R) % (BM // 2) == 0
+
+
+SCHEDULE_SHAPES = [
+    (4096, 4096, 4, 0, 128, 128), (4096, 4096, 4, 2, 128, 128), (8192, 7168, 8, 0, 128, 128),
+    (1024, 7168, 8, 5, 128, 128), (256, 7168, 8, 0, 128, 128), (256, 512, 2, 1, 128, 128),
+    (384, 520, 3, 1, 64, 64), (640, 264, 5, 4, 64, 8), (200, 520, 2, 1, 32, 64), (640, 384, 1, 0, 128, 128),
+    (520, 1032, 8, 4, 128, 128), (1536, 136, 6, 3, 128, 8),
+]
+
+
+@pytest.mark.parametrize("M,N,R,owner,ftm,ftn", SCHEDULE_SHAPES)
+def test_schedule_covers_every_output_once(M, N, R, owner, ftm, ftn):
+    seg = M // R
+    for base, (BM, BN) in TILE_DIMS.items():
+        for tile in (base, base | A.TILE_CONTIGUOUS_ROWS):
+            for publish in (False, True):
+                if A.gemm_rs_supports(M, N, 64, R, owner, ftm, ftn, publish=publish, tile=tile) != 0:
+                    continue
+                sched = A.gemm_rs_schedule(M, N, 64, R, owner, ftm, ftn, publish=publish, tile=tile)
+                ncb = -(-N // BN)
+                seen = np.zeros((M, ncb), np.int32)
+                blocks = set()
+                paired = False
+                for rb, cb, a0, alen, b0, blen in sched:
+                    blocks.add((rb, cb))
+                    assert 0 <= cb < ncb
+                    for first, n in ((a0, alen), (b0, blen)):
+                        assert 0 <= n <= BM
+                        if n:
+                            seen[first:first + n, cb] += 1
+                    if b0 != a0 + alen and blen:
+                        paired = True
+                assert len(blocks) == len(sched), "a tile is launched twice"
+                assert np.all(seen == 1), (tile, publish, "rows covered %s times" % np.unique(seen))
+                if paired:
+                    CK = BM // 2
+                    assert paired_eligible(M, R, BM) and not tile & A.TILE_CONTIGUOUS_ROWS
+                    for rb, cb, a0, alen, b0, blen in sched:
+                        for first, n in ((a0, alen), (b0, blen)):
+                            # a chunk is a whole half-block inside one segment
+                            assert n in (0, CK) and (n == 0 or first // seg == (first + n - 1) // seg)
+                        # at most one owner chunk per workgroup: the owner rows are spread out
+                        own = sum(1 for first, n in ((a0, alen), (b0, blen)) if n and first // seg == owner)
+                        assert own <= 1 or R == 1
 
 
 def test_auto_tile_is_supported():
@@ -151,3 +207,16 @@ def test_binding_checks_dtype_before_pointers():
     x = torch.zeros(4, 8, dtype=torch.float32)
     with pytest.raises(TypeError):
         A.combine_reduce(x, x, x)
+
+
+@pytest.mark.parametrize("M,N,R", [(4096, 4096, 4), (8192, 7168, 8), (4096, 7168, 8)])
+def test_owner_half_blocks_are_paired_on_the_model_shapes(M, N, R):
+    seg = M // R
+    tile = A.gemm_rs_pick_tile(M, N, 2048, R, 0, publish=True)
+    BM = A.TILE_DIMS[tile][0]
+    sched = A.gemm_rs_schedule(M, N, 2048, R, 0, publish=True, tile=tile)
+    owner_wgs = [s for s in sched if s[2] // seg == 0 or (s[5] and s[4] // seg == 0)]
+    # every workgroup holding owner rows holds exactly one half-block of them, next to a non-owner one
+    assert len(owner_wgs) == (seg // (BM // 2)) * (-(-N // A.TILE_DIMS[tile][1]))
+    for rb, cb, a0, alen, b0, blen in owner_wgs:
+        assert a0 // seg == 0 and alen == BM // 2 and blen == BM // 2 and b0 // seg != 0

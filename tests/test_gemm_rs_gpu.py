@@ -45,11 +45,11 @@ def run(case, tile=A.TILE_AUTO, publish=True, ftm=128, ftn=128, stream=None, sta
     return res
 
 
-def check_against_oracle(case, res, ftm=128, ftn=128, rows=None, what=""):
+def check_against_oracle(case, res, ftm=128, ftn=128, rows=None, what="", ref=None):
     M, N, R, owner = case["M"], case["N"], case["R"], case["owner"]
     seg = M // R
     if rows is None:
-        ref_out, ref_send = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
+        ref_out, ref_send = ref if ref is not None else oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
         assert_bf16_close(res["out"], ref_out, what + " out")
         if res["send"] is not None:
             mask = np.ones(M, bool)
@@ -70,19 +70,28 @@ def check_against_oracle(case, res, ftm=128, ftn=128, rows=None, what=""):
 
 
 def tiles_to_try(case, ftm, ftn):
-    for t in sorted(A.TILE_NAMES):
-        pub = A.gemm_rs_supports(case["M"], case["N"], case["K"], case["R"], case["owner"], ftm, ftn,
-                                 publish=True, tile=t) == 0
-        yield t, pub
+    """Every tile, and its contiguous-rows form where that is a different row layout."""
+    for base in sorted(A.TILE_NAMES):
+        variants = [base]
+        if A.TILE_DIMS[base][0] >= 64:
+            variants.append(base | A.TILE_CONTIGUOUS_ROWS)
+        for t in variants:
+            pub = A.gemm_rs_supports(case["M"], case["N"], case["K"], case["R"], case["owner"], ftm, ftn,
+                                     publish=True, tile=t) == 0
+            yield t, pub
+
+
+def tile_name(t):
+    return A.TILE_NAMES[t & ~A.TILE_CONTIGUOUS_ROWS] + ("/contiguous" if t & A.TILE_CONTIGUOUS_ROWS else "")
 
 
 @pytest.mark.parametrize("owner", [0, 1])
 def test_tiny_workload_every_tile(owner):
     case = inputs.workload_gemm_rs(1, owner=owner)
     for tile, pub in tiles_to_try(case, 128, 128):
-        print("tiny workload owner=%d tile=%s publish=%s" % (owner, A.TILE_NAMES[tile], pub), flush=True)
+        print("tiny workload owner=%d tile=%s publish=%s" % (owner, tile_name(tile), pub), flush=True)
         res = run(case, tile=tile, publish=pub)
-        check_against_oracle(case, res, what="tiny/%s" % A.TILE_NAMES[tile])
+        check_against_oracle(case, res, what="tiny/%s" % tile_name(tile))
 
 
 @pytest.mark.parametrize("M,N,K,R,owner,ftm,ftn", [
@@ -96,9 +105,24 @@ def test_tiny_workload_every_tile(owner):
 def test_ragged_shapes_every_tile(M, N, K, R, owner, ftm, ftn):
     case = inputs.gemm_rs_case(M, N, K, R, owner=owner, seed=7 + M + N + K)
     for tile, pub in tiles_to_try(case, ftm, ftn):
-        print("ragged %s tile=%s publish=%s" % ((M, N, K, R, owner), A.TILE_NAMES[tile], pub), flush=True)
+        print("ragged %s tile=%s publish=%s" % ((M, N, K, R, owner), tile_name(tile), pub), flush=True)
         res = run(case, tile=tile, publish=pub, ftm=ftm, ftn=ftn)
-        check_against_oracle(case, res, ftm, ftn, what="ragged/%s" % A.TILE_NAMES[tile])
+        check_against_oracle(case, res, ftm, ftn, what="ragged/%s" % tile_name(tile))
+
+
+@pytest.mark.parametrize("M,N,K,R,owner,ftm,ftn", [
+    (512, 520, 136, 4, 1, 64, 64),     # half-blocks of 128 / 64 rows, N tail
+    (384, 264, 72, 3, 2, 128, 8),      # R=3: one non-owner half-block left unpaired
+    (640, 1032, 200, 5, 3, 64, 128),   # R=5: pure, single and owner-paired blocks
+    (2048, 7168, 256, 8, 5, 128, 128), # R=8 at the model width
+])
+def test_paired_half_blocks_every_tile(M, N, K, R, owner, ftm, ftn):
+    case = inputs.gemm_rs_case(M, N, K, R, owner=owner, seed=11 + M + N + K)
+    ref = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
+    for tile, pub in tiles_to_try(case, ftm, ftn):
+        print("paired %s tile=%s publish=%s" % ((M, N, K, R, owner), tile_name(tile), pub), flush=True)
+        res = run(case, tile=tile, publish=pub, ftm=ftm, ftn=ftn)
+        check_against_oracle(case, res, ftm, ftn, what="paired/%s" % tile_name(tile), ref=ref)
 
 
 def test_golden_all_ones_two_ranks_on_gpu():
