@@ -23,6 +23,7 @@ struct EmuParams {
 };
 
 __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
+    // one workgroup of 256 threads per (peer, flag tile) item
     const int peer = p.order[2 * (int64_t)blockIdx.x];
     const int64_t t = p.order[2 * (int64_t)blockIdx.x + 1];
     const bool valid = peer >= 0 && peer < p.R && peer != p.owner && t >= 0 && t < p.ftiles;
@@ -38,9 +39,20 @@ __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
             s = p.src[i];
             d = p.recv[i];
         }
-    for (int64_t i = threadIdx.x; i < rows * packs; i += blockDim.x) {
-        const int64_t off = (r0 + i / packs) * p.N + c0 + (i % packs) * 8;
-        *reinterpret_cast<uint4 *>(d + off) = *reinterpret_cast<const uint4 *>(s + off);
+    // 16-byte packs, eight per thread in flight (streaming loads and stores)
+    const int ppr = (int)packs, total = (int)rows * ppr;
+    for (int base = 0; base < total; base += 256 * 8) {
+        uint4 v[8];
+        int64_t off[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int i = base + (int)threadIdx.x + k * 256;
+            off[k] = i < total ? (r0 + i / ppr) * p.N + c0 + (i % ppr) * 8 : -1;
+            if (off[k] >= 0) v[k] = load16_nt(s + off[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (off[k] >= 0) store16_nt(d + off[k], v[k]);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();

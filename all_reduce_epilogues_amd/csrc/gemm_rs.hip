@@ -183,7 +183,7 @@ constexpr int lds_bytes() { return S * (BM * BK * 2 + BK * BN * 2); }
 // all of them through vector registers).
 enum { kNoOwnerRows = 0, kOwnerChunkA = 1, kOwnerRowsAnywhere = 2 };
 
-template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, int KIND>
+template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, int KIND, bool WT>
 __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *smem, int rb, int cb, int64_t a0,
                                              int alen, int64_t b0, int blen) {
     constexpr int NWN = BN / WN;
@@ -205,7 +205,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     static_assert(CH == 4 || CH == 8, "BK must be 32 or 64");
     static_assert(A_INSTR >= 1 && A_INSTR * NW * 1024 == A_BYTES, "X stage split");
     static_assert(B_INSTR >= 1 && B_INSTR * NW * 1024 == B_BYTES, "W stage split");
-    static_assert(B_CPR >= 16 && B_CPR <= 64, "W swizzle needs 16..64 chunks per row");
+    static_assert(WT || (B_CPR >= 16 && B_CPR <= 64), "W swizzle needs 16..64 chunks per row");
     static_assert(NW * ER * EPS * 4 <= LDS_BYTES, "epilogue slabs must fit the stage memory");
     static_assert(S >= 2 && (S - 2) * NDMA < 64, "stage count vs vmcnt range");
 
@@ -244,7 +244,9 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     // or N get an out-of-range offset); k0 goes into the scalar offset.
     auto a_row_of = [&](int i) { return (wave * A_INSTR + i) * A_RPI + lane / CH; };
     auto a_col_of = [&](int i) { return ((lane % CH) ^ swz_a<CH>(a_row_of(i))) * 8; };
-    auto b_row_of = [&](int i) { return (wave * B_INSTR + i) * B_RPI + lane / B_CPR; };
+    // (W stored as [N,K] (WT): its tile is K-contiguous like X's, same layout and swizzle)
+    auto b_row_of = [&](int i) { return WT ? (wave * B_INSTR + i) * A_RPI + lane / CH : (wave * B_INSTR + i) * B_RPI + lane / B_CPR; };
+    auto b_col_of = [&](int i) { return ((lane % CH) ^ swz_a<CH>(b_row_of(i))) * 8; };  // WT only
     uint32_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
@@ -253,10 +255,19 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     }
 #pragma unroll
     for (int i = 0; i < B_INSTR; ++i) {
-        const int r = b_row_of(i);
-        const int64_t gn = n0 + ((lane % B_CPR) ^ swz_b(r)) * 8;
-        b_off[i] = (gn < N) ? (uint32_t)((r * N + gn) * 2) : kOob;
+        if constexpr (WT) {
+            const int64_t gn = n0 + b_row_of(i);
+            b_off[i] = (gn < N) ? (uint32_t)((gn * K + b_col_of(i)) * 2) : kOob;
+        } else {
+            const int r = b_row_of(i);
+            const int64_t gn = n0 + ((lane % B_CPR) ^ swz_b(r)) * 8;
+            b_off[i] = (gn < N) ? (uint32_t)((r * N + gn) * 2) : kOob;
+        }
     }
+    // byte step of W per k (soffset per K step) and whether lane's W k is in range
+    constexpr int64_t one = 1;
+    const int64_t w_kstride = WT ? 2 * one : N * 2;
+    auto b_k_of = [&](int i) { return WT ? b_col_of(i) : b_row_of(i); };
 
     lds_t *const S0 = (lds_t *)smem;
     auto lds_addr = [](const lds_t *ptr) { return (uint32_t)(uintptr_t)ptr; };
@@ -270,7 +281,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         const uint32_t lb = lds_addr(st + A_BYTES) + wave_u * B_INSTR * 1024;
         const int64_t k0 = (int64_t)kt * BK;
         if (k0 + BK <= K) {  // full step: precomputed offsets, k0 in soffset
-            const uint32_t sa = (uint32_t)(k0 * 2), sb = (uint32_t)(k0 * N * 2);
+            const uint32_t sa = (uint32_t)(k0 * 2), sb = (uint32_t)(k0 * w_kstride);
 #pragma unroll
             for (int i = 0; i < A_INSTR; ++i) dma16(xr, la + i * 1024, a_off[i], sa);
 #pragma unroll
@@ -283,9 +294,40 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
             }
 #pragma unroll
             for (int i = 0; i < B_INSTR; ++i) {
-                const bool in = b_off[i] != kOob && k0 + b_row_of(i) < K;
-                dma16(wr, lb + i * 1024, in ? b_off[i] + (uint32_t)(k0 * N * 2) : kOob, 0);
+                const bool in = b_off[i] != kOob && k0 + b_k_of(i) < K;
+                dma16(wr, lb + i * 1024, in ? b_off[i] + (uint32_t)(k0 * w_kstride) : kOob, 0);
             }
+        }
+    };
+    // The same loads one instruction at a time (d < NDMA), so that they can be
+    // spread between the MFMAs of a step.
+    struct StepLoads {
+        uint32_t la, lb, sa, sb;
+        int64_t k0;
+        bool full;
+    };
+    auto step_loads = [&](int kt) {
+        const lds_t *st = S0 + (kt % S) * STAGE;
+        StepLoads sl;
+        sl.la = lds_addr(st) + wave_u * A_INSTR * 1024;
+        sl.lb = lds_addr(st + A_BYTES) + wave_u * B_INSTR * 1024;
+        sl.k0 = (int64_t)kt * BK;
+        sl.full = sl.k0 + BK <= K;
+        sl.sa = sl.full ? (uint32_t)(sl.k0 * 2) : 0u;
+        sl.sb = sl.full ? (uint32_t)(sl.k0 * w_kstride) : 0u;
+        return sl;
+    };
+    auto issue_one = [&](const StepLoads &sl, int d) {
+        if (d < A_INSTR) {
+            const int i = d;
+            const bool in = a_off[i] != kOob && sl.k0 + a_col_of(i) < K;
+            const uint32_t vo = sl.full ? a_off[i] : in ? a_off[i] + (uint32_t)(sl.k0 * 2) : kOob;
+            dma16(xr, sl.la + i * 1024, vo, sl.sa);
+        } else {
+            const int i = d - A_INSTR;
+            const bool in = b_off[i] != kOob && sl.k0 + b_k_of(i) < K;
+            const uint32_t vo = sl.full ? b_off[i] : in ? b_off[i] + (uint32_t)(sl.k0 * w_kstride) : kOob;
+            dma16(wr, sl.lb + i * 1024, vo, sl.sb);
         }
     };
     // wait until this wave's loads of the oldest outstanding step have landed,
@@ -319,6 +361,12 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
+            if constexpr (WT) {
+                const int r = wn * WN + j * 32 + (lane & 31);
+                const int c = kk * 2 + (lane >> 5);
+                f.b[j] = *(const __attribute__((address_space(3))) bf16x8 *)(Bs + r * (BK * 2) + ((c ^ swz_a<CH>(r)) << 4));
+                continue;
+            }
             const int n = wn * WN + j * 32 + b_n_lane;
             bf16x4 h[2];
 #pragma unroll
@@ -331,6 +379,47 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
             f.b[j] = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
         }
     };
+    // Operand reads of piece pc (of TM): A row block pc and the W columns j
+    // with j*TM/TN == pc.
+    auto load_frag_piece = [&](const lds_t *As, int kk, Frag &f, int pc) {
+        const lds_t *Bs = As + A_BYTES;
+        {
+            const int i = pc;
+            const int r = wm * WM + i * 32 + (lane & 31);
+            const int c = kk * 2 + (lane >> 5);
+            f.a[i] = *(const __attribute__((address_space(3))) bf16x8 *)(As + r * (BK * 2) + ((c ^ swz_a<CH>(r)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            if ((j * TM) / TN != pc) continue;
+            if constexpr (WT) {
+                const int r = wn * WN + j * 32 + (lane & 31);
+                const int c = kk * 2 + (lane >> 5);
+                f.b[j] = *(const __attribute__((address_space(3))) bf16x8 *)(Bs + r * (BK * 2) + ((c ^ swz_a<CH>(r)) << 4));
+                continue;
+            }
+            const int n = wn * WN + j * 32 + b_n_lane;
+            bf16x4 h[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int k = kk * 16 + b_k_lane + 4 * half;
+                const lds_t *src = Bs + k * (BN * 2) + (((n >> 3) ^ swz_b(k)) << 4) + (n & 7) * 2;
+                h[half] = __builtin_bit_cast(
+                    bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)src));
+            }
+            f.b[j] = __builtin_shufflevector(h[0], h[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+    };
+    auto reads_in_piece = [](int pc) {
+        int n = 1;
+        for (int j = 0; j < TN; ++j) n += ((j * TM) / TN == pc) ? (WT ? 1 : 2) : 0;
+        return n;
+    };
+    auto mma_row = [&](const Frag &f, int i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+    };
     auto mma = [&](const Frag &f) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -341,10 +430,15 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     // Scheduling groups: after each MFMA one LDS operand read, so the reads of
     // the next sub-step overlap the MFMAs of the current one (the compiler's
     // default is to drain each read right before its first use).
-    constexpr int NREAD = TM + 2 * TN;  // LDS reads per sub-step
+    constexpr int NREAD = TM + (WT ? 1 : 2) * TN;  // LDS reads per sub-step
     constexpr int NMMA = TM * TN;       // MFMAs per sub-step
     constexpr int NK = BK / 16;         // MFMA sub-steps per K step
     static_assert(NK % 2 == 0, "sub-step parity must repeat across K steps");
+#ifndef AREPI_SPREAD_LOADS
+#define AREPI_SPREAD_LOADS 1
+#endif
+    constexpr bool kSpreadLoads = AREPI_SPREAD_LOADS != 0 && S >= 3;
+    constexpr int kHalf = (NDMA + 1) / 2;  // loads of a step issued before its stage barrier
     auto interleave = [&]() {
 #pragma unroll
         for (int n = 0; n < NMMA; ++n) {
@@ -370,19 +464,55 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     load_frag(S0, 0, f[0]);
     for (int t = 0; t < KT; ++t) {
         const lds_t *X = S0 + (t % S) * STAGE;
-        issue_step(t + S - 1);
+        if constexpr (kSpreadLoads) {
+            // Step t+S-1's loads are spread over the step: the first and the
+            // last sub-step run in TM pieces (one MFMA row plus its share of the
+            // next operand reads), each piece followed by its share of the
+            // loads (half of them before the stage barrier, half after).
+            const StepLoads sl = step_loads(t + S - 1);
+            auto pieces = [&](const lds_t *src, int kk_next, Frag &fn, const Frag &fc, int d0) {
 #pragma unroll
-        for (int kk = 0; kk + 1 < NK; ++kk) {
-            load_frag(X, kk + 1, f[(kk + 1) & 1]);
-            mma(f[kk & 1]);
+                for (int pc = 0; pc < TM; ++pc) {
+                    load_frag_piece(src, kk_next, fn, pc);
+                    mma_row(fc, pc);
+#pragma unroll
+                    for (int n = 0; n < TN; ++n) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                        if (n < reads_in_piece(pc)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int d = d0 + (pc * kHalf) / TM; d < d0 + ((pc + 1) * kHalf) / TM; ++d)
+                        if (d < NDMA) issue_one(sl, d);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            pieces(X, 1, f[1], f[0], 0);
+#pragma unroll
+            for (int kk = 1; kk + 1 < NK; ++kk) {
+                load_frag(X, kk + 1, f[(kk + 1) & 1]);
+                mma(f[kk & 1]);
+                interleave();
+            }
+            // step t+1's loads are done once at most the younger ones are in flight
+            wait_vmcnt<(S - 3) * NDMA + kHalf>();
+            __syncthreads();
+            pieces(S0 + ((t + 1) % S) * STAGE, 0, f[0], f[(NK - 1) & 1], kHalf);
+        } else {
+            issue_step(t + S - 1);
+#pragma unroll
+            for (int kk = 0; kk + 1 < NK; ++kk) {
+                load_frag(X, kk + 1, f[(kk + 1) & 1]);
+                mma(f[kk & 1]);
+                interleave();
+            }
+            wait_oldest_step();
+            __syncthreads();
+            // (after the last step this reads operands that are never used)
+            load_frag(S0 + ((t + 1) % S) * STAGE, 0, f[0]);
+            mma(f[(NK - 1) & 1]);
             interleave();
         }
-        wait_oldest_step();
-        __syncthreads();
-        // (after the last step this reads operands that are never used)
-        load_frag(S0 + ((t + 1) % S) * STAGE, 0, f[0]);
-        mma(f[(NK - 1) & 1]);
-        interleave();
     }
     wait_vmcnt_zero();
     __syncthreads();  // the stages are reused by the epilogue below
@@ -657,7 +787,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
 
 // WPE: waves per SIMD the register allocation targets (1 = one big-tile
 // workgroup per CU; 2 = two co-resident workgroups; 0 = no target).
-template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS>
+template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, bool WT>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, WPE > 0 ? WPE : 8)))
     gemm_rs_kernel(const GemmRsParams p) {
@@ -672,11 +802,11 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     const bool own_a = alen > 0 && a0 < oseg1 && a0 + alen > oseg0;
     const bool own_b = blen > 0 && b0 < oseg1 && b0 + blen > oseg0;
     if (!own_a && !own_b)
-        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kNoOwnerRows>(p, smem, rb, cb, a0, alen, b0, blen);
+        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kNoOwnerRows, WT>(p, smem, rb, cb, a0, alen, b0, blen);
     else if (p.paired)  // paired half-blocks: only chunk A can be an owner chunk
-        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerChunkA>(p, smem, rb, cb, a0, alen, b0, blen);
+        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerChunkA, WT>(p, smem, rb, cb, a0, alen, b0, blen);
     else
-        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerRowsAnywhere>(p, smem, rb, cb, a0, alen, b0, blen);
+        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerRowsAnywhere, WT>(p, smem, rb, cb, a0, alen, b0, blen);
 }
 
 // ---- host side --------------------------------------------------------------------
@@ -686,14 +816,15 @@ struct TileCfg {
     int slots;   // workgroups co-resident on one CU (LDS / register bound)
     double eff;  // relative per-CU throughput used by the automatic choice
 };
-// eff: sustained per-CU throughput relative to the best tile, from timing the
-// tp=4 / tp=8 workloads on MI355X; cost = waves of tiles x tile area / eff.
+// eff: sustained per-CU throughput relative to the 4-stage 256x256 tile, from
+// timing the tp=4 / tp=8 workloads on MI355X (contiguous rows).
 constexpr TileCfg kTiles[] = {
+    {AREPI_TILE_256x256_W8, 256, 256, 1, 1.08},
     {AREPI_TILE_256x256_S4, 256, 256, 1, 1.00},
-    {AREPI_TILE_128x256_S3, 128, 256, 2, 0.98},
-    {AREPI_TILE_256x128_S3, 256, 128, 2, 0.97},
-    {AREPI_TILE_256x256, 256, 256, 1, 0.93},
-    {AREPI_TILE_128x128_S4, 128, 128, 2, 0.82},
+    {AREPI_TILE_256x256, 256, 256, 1, 0.96},
+    {AREPI_TILE_256x128_S3, 256, 128, 2, 0.95},
+    {AREPI_TILE_128x256_S3, 128, 256, 2, 0.93},
+    {AREPI_TILE_128x128_S4, 128, 128, 2, 0.80},
     {AREPI_TILE_128x256, 128, 256, 1, 0.80},
     {AREPI_TILE_128x128, 128, 128, 2, 0.75},
     {AREPI_TILE_64x128, 64, 128, 3, 0.60},
@@ -761,12 +892,13 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool pub
     int best = -1;
     double best_cost = 0;
     for (const auto &t : kTiles) {
-        if (publish && !flags_nest(M, N, R, ftm, ftn, t.BM, t.BN) &&
-            !use_paired(M, N, R, ftm, ftn, t.BM, t.BN, true, false))
-            continue;
+        if (publish && !flags_nest(M, N, R, ftm, ftn, t.BM, t.BN)) continue;
         const int64_t count = cdiv(M, t.BM) * cdiv(N, t.BN);
-        // waves of co-resident tiles x work per CU per wave / efficiency
-        const double cost = (double)cdiv(count, 256 * t.slots) * t.slots * t.BM * t.BN / t.eff;
+        // waves of co-resident tiles x time of one wave; a wave with fewer
+        // tiles than slots on each CU runs fewer of them side by side
+        const int64_t waves = cdiv(count, 256 * (int64_t)t.slots);
+        const int64_t per_cu = std::min<int64_t>(t.slots, cdiv(count, 256));
+        const double cost = (double)waves * per_cu * t.BM * t.BN / t.eff;
         if (best < 0 || cost < best_cost) {
             best = t.id;
             best_cost = cost;
@@ -811,15 +943,19 @@ int plan(GemmRsParams &p, const TileCfg *t, int64_t M, int64_t N, int64_t K, int
     return AREPI_OK;
 }
 
+#ifndef AREPI_EXP_WT
+#define AREPI_EXP_WT 0
+#endif
 template <int BM, int BN, int WM, int WN, int BK, int S, int WPE>
 void launch(const GemmRsParams &p, hipStream_t stream) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
+    constexpr bool WT = AREPI_EXP_WT != 0;
     if (p.npeers <= 1)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1>), dim3(p.nWG), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1, WT>), dim3(p.nWG), dim3(NT), 0, stream, p);
     else if (p.npeers <= 3)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3>), dim3(p.nWG), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3, WT>), dim3(p.nWG), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1>), dim3(p.nWG), dim3(NT), 0,
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1, WT>), dim3(p.nWG), dim3(NT), 0,
                            stream, p);
 }
 
@@ -858,8 +994,8 @@ extern "C" int arepi_gemm_rs_supports(int64_t M, int64_t N, int64_t K, int R, in
         rc = arepi_gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish);
         return rc < 0 ? rc : ok();
     }
-    const bool contiguous = (tile_cfg & AREPI_TILE_CONTIGUOUS_ROWS) != 0;
-    const int id = tile_cfg & ~AREPI_TILE_CONTIGUOUS_ROWS;
+    const bool contiguous = (tile_cfg & AREPI_TILE_PAIRED_ROWS) == 0;
+    const int id = tile_cfg & ~AREPI_TILE_PAIRED_ROWS;
     const TileCfg *t = id == AREPI_TILE_AUTO ? nullptr : find_tile(id);
     if (!t) return fail(AREPI_EINVAL, "arepi_gemm_rs: tile_cfg=" + std::to_string(tile_cfg) + " is not an AREPI_TILE_* value");
     if (publish && !flags_nest(M, N, R, flag_tile_m, flag_tile_n, t->BM, t->BN) &&
@@ -894,9 +1030,9 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
             if (!aligned16(recv[p])) return bad("recv[" + std::to_string(p) + "] must be 16-byte aligned");
         }
     }
-    const bool contiguous = (tile_cfg & AREPI_TILE_CONTIGUOUS_ROWS) != 0;
+    const bool contiguous = (tile_cfg & AREPI_TILE_PAIRED_ROWS) == 0;
     const int cfg = tile_cfg == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, flag_tile_m, flag_tile_n, publish)
-                                                : tile_cfg & ~AREPI_TILE_CONTIGUOUS_ROWS;
+                                                : tile_cfg & ~AREPI_TILE_PAIRED_ROWS;
     const TileCfg *t = find_tile(cfg);
 
     GemmRsParams p{};
@@ -926,6 +1062,7 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
         case AREPI_TILE_256x128_S3: launch<256, 128, 128, 64, 32, 3, 2>(p, s); break;
         case AREPI_TILE_128x256_S3: launch<128, 256, 64, 128, 32, 3, 2>(p, s); break;
         case AREPI_TILE_128x128_S4: launch<128, 128, 64, 64, 32, 4, 2>(p, s); break;
+        case AREPI_TILE_256x256_W8: launch<256, 256, 128, 64, 32, 4, 2>(p, s); break;
         default: return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_fused: no kernel for tile " + std::to_string(cfg));
     }
     return check_launch("arepi_gemm_rs_fused");
@@ -936,9 +1073,9 @@ extern "C" int64_t arepi_gemm_rs_schedule(int64_t M, int64_t N, int64_t K, int R
                                           int64_t capacity) {
     int rc = arepi_gemm_rs_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish, tile_cfg);
     if (rc) return rc;
-    const bool contiguous = (tile_cfg & AREPI_TILE_CONTIGUOUS_ROWS) != 0;
+    const bool contiguous = (tile_cfg & AREPI_TILE_PAIRED_ROWS) == 0;
     const int cfg = tile_cfg == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, flag_tile_m, flag_tile_n, publish != 0)
-                                                : tile_cfg & ~AREPI_TILE_CONTIGUOUS_ROWS;
+                                                : tile_cfg & ~AREPI_TILE_PAIRED_ROWS;
     const TileCfg *t = find_tile(cfg);
     GemmRsParams p{};
     rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, publish != 0, contiguous);

@@ -75,19 +75,21 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
     ev_clear = [torch.cuda.Event() for _ in range(n_ev)]
 
     def step(i):
-        # the previous step's GEMM must be done reading ready_in before it is cleared
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            rin.zero_()
-        ev_clear[i].record(side)
+        # Each step: clear ready_in on the main stream (after the previous GEMM,
+        # which could only finish once every bit of the previous producer had
+        # landed), then the GEMM on the main stream and the producer on the side
+        # stream run concurrently; the GEMM's owner tiles wait for the
+        # producer's bits.  ready_out is only ever OR-ed into: no clearing.
+        # (The producer's waves share CUs with the GEMM's: the chosen tile
+        # leaves the registers for them.)
+        rin.zero_()
+        ev_clear[i].record(main)
+        side.wait_event(ev_clear[i])
         A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, owner, M, N, stream=side)
-        main.wait_event(ev_clear[i])
-        rout.zero_()
         ev_gs[i].record(main)
         A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile,
                         status=status, stream=main)
         ev_ge[i].record(main)
-        main.wait_stream(side)
 
     for i in range(warmup):
         step(i)
@@ -268,8 +270,9 @@ def main():
         secondary["lamport_ar_rmsnorm"] = lamport(A, inputs, torch, max(10, a.steps // 2), 3)
     if a.only in (None, "combine"):
         secondary["combine_reduce"] = combine(A, inputs, torch, max(10, a.steps // 2), 3)
-    if a.sweep:
+    if a.only in (None, "gemm_rs"):
         secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2)
+    if a.sweep:
         secondary["gemm_rs_tp8_sweep"] = [gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 3, M=m)
                                          for m in inputs.TP8_M_SWEEP]
     line = {

@@ -68,12 +68,14 @@ enum {
     AREPI_TILE_256x128_S3 = 7,
     AREPI_TILE_128x256_S3 = 8,
     AREPI_TILE_128x128_S4 = 9,
-    /* ORed into an explicit tile: keep each workgroup's rows one contiguous
-     * block.  Otherwise, when every segment is a whole number of half-blocks,
-     * a workgroup takes two half-blocks (BM/2 rows each, BM >= 64) and the
-     * owner segment's half-blocks are each paired with a non-owner one, which
-     * spreads the owner rows' peer reads over twice as many workgroups. */
-    AREPI_TILE_CONTIGUOUS_ROWS = 0x100
+    AREPI_TILE_256x256_W8 = 10, /* 8 waves (two per SIMD), BK 32, 4 stages */
+    /* ORed into an explicit tile: when every segment is a whole number of
+     * half-blocks (BM/2 rows, BM >= 64), a workgroup takes two half-blocks and
+     * the owner segment's half-blocks are each paired with a non-owner one,
+     * which spreads the owner rows' peer reads over twice as many workgroups.
+     * Without it (and for other shapes) each workgroup's rows are one
+     * contiguous block. */
+    AREPI_TILE_PAIRED_ROWS = 0x200
 };
 
 /* Message describing the last failed call on this thread ("" if none). */

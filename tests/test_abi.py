@@ -65,10 +65,10 @@ TILE_DIMS = A.TILE_DIMS
 def test_supports_matches_flag_nesting(M, N, R, ftm, ftn):
     for tile, (BM, BN) in TILE_DIMS.items():
         # contiguous row blocks: flag tiles must nest in BM x BN blocks
-        rc = A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=True, tile=tile | A.TILE_CONTIGUOUS_ROWS)
+        rc = A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=True, tile=tile)
         assert (rc == 0) == nests(M, N, R, ftm, ftn, BM, BN), (tile, A.last_error())
         # paired half-blocks are a second way to nest them
-        rc = A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=True, tile=tile)
+        rc = A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=True, tile=tile | A.TILE_PAIRED_ROWS)
         expect = nests(M, N, R, ftm, ftn, BM, BN) or (paired_eligible(M, R, BM) and
                                                       nests(M, N, R, ftm, ftn, BM // 2, BN))
         assert (rc == 0) == expect, (tile, A.last_error())
@@ -93,7 +93,7 @@ SCHEDULE_SHAPES = [
 def test_schedule_covers_every_output_once(M, N, R, owner, ftm, ftn):
     seg = M // R
     for base, (BM, BN) in TILE_DIMS.items():
-        for tile in (base, base | A.TILE_CONTIGUOUS_ROWS):
+        for tile in (base, base | A.TILE_PAIRED_ROWS):
             for publish in (False, True):
                 if A.gemm_rs_supports(M, N, 64, R, owner, ftm, ftn, publish=publish, tile=tile) != 0:
                     continue
@@ -115,7 +115,7 @@ def test_schedule_covers_every_output_once(M, N, R, owner, ftm, ftn):
                 assert np.all(seen == 1), (tile, publish, "rows covered %s times" % np.unique(seen))
                 if paired:
                     CK = BM // 2
-                    assert paired_eligible(M, R, BM) and not tile & A.TILE_CONTIGUOUS_ROWS
+                    assert paired_eligible(M, R, BM) and tile & A.TILE_PAIRED_ROWS
                     for rb, cb, a0, alen, b0, blen in sched:
                         for first, n in ((a0, alen), (b0, blen)):
                             # a chunk is a whole half-block inside one segment
@@ -210,11 +210,11 @@ def test_binding_checks_dtype_before_pointers():
 
 
 @pytest.mark.parametrize("M,N,R", [(4096, 4096, 4), (8192, 7168, 8), (4096, 7168, 8)])
-def test_owner_half_blocks_are_paired_on_the_model_shapes(M, N, R):
+def test_owner_half_blocks_pair_on_the_model_shapes(M, N, R):
     seg = M // R
     tile = A.gemm_rs_pick_tile(M, N, 2048, R, 0, publish=True)
     BM = A.TILE_DIMS[tile][0]
-    sched = A.gemm_rs_schedule(M, N, 2048, R, 0, publish=True, tile=tile)
+    sched = A.gemm_rs_schedule(M, N, 2048, R, 0, publish=True, tile=tile | A.TILE_PAIRED_ROWS)
     owner_wgs = [s for s in sched if s[2] // seg == 0 or (s[5] and s[4] // seg == 0)]
     # every workgroup holding owner rows holds exactly one half-block of them, next to a non-owner one
     assert len(owner_wgs) == (seg // (BM // 2)) * (-(-N // A.TILE_DIMS[tile][1]))

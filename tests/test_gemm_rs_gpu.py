@@ -70,11 +70,11 @@ def check_against_oracle(case, res, ftm=128, ftn=128, rows=None, what="", ref=No
 
 
 def tiles_to_try(case, ftm, ftn):
-    """Every tile, and its contiguous-rows form where that is a different row layout."""
+    """Every tile, and its paired-half-blocks form where that is a different row layout."""
     for base in sorted(A.TILE_NAMES):
         variants = [base]
         if A.TILE_DIMS[base][0] >= 64:
-            variants.append(base | A.TILE_CONTIGUOUS_ROWS)
+            variants.append(base | A.TILE_PAIRED_ROWS)
         for t in variants:
             pub = A.gemm_rs_supports(case["M"], case["N"], case["K"], case["R"], case["owner"], ftm, ftn,
                                      publish=True, tile=t) == 0
@@ -82,7 +82,7 @@ def tiles_to_try(case, ftm, ftn):
 
 
 def tile_name(t):
-    return A.TILE_NAMES[t & ~A.TILE_CONTIGUOUS_ROWS] + ("/contiguous" if t & A.TILE_CONTIGUOUS_ROWS else "")
+    return A.TILE_NAMES[t & ~A.TILE_PAIRED_ROWS] + ("/paired" if t & A.TILE_PAIRED_ROWS else "")
 
 
 @pytest.mark.parametrize("owner", [0, 1])
