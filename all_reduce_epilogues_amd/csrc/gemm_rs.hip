@@ -9,27 +9,34 @@
 // stored as this rank's outgoing partials.
 //
 // Design (gfx950, not a translation of the pages' sm100 / FlyDSL kernels):
-//  * Workgroup tile BM x BN, 4 waves of 64 lanes, each wave a WM x WN block of
-//    32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulators).
-//  * K is walked in BK = 64 steps through a two-stage LDS ring: the next
-//    step's global loads are issued into registers before the current step's
-//    MFMAs and written to the other LDS stage after them, one barrier per step.
-//  * X [M,K] is K-contiguous and goes to LDS as is.  W [K,N] is N-contiguous;
-//    each thread loads a 4(k) x 8(n) block and transposes it in registers so
-//    the LDS copy is K-contiguous per column, which is what the MFMA B operand
-//    reads (8 consecutive k per lane).
-//  * LDS rows are 128 bytes (64 bf16); the eight 16-byte chunks of a row are
-//    XOR-swizzled by (row ^ row>>3) & 7 so that both the 16-byte MFMA operand
-//    reads (32 consecutive rows, one chunk) and the 16-byte X writes avoid
-//    bank conflicts.
-//  * Epilogue: the accumulators (4 consecutive rows per lane in the MFMA
-//    layout) are staged through LDS one 32-row slab at a time and read back
-//    row-contiguous, so every global access is a 16-byte, row-coalesced pack.
-//    Owner rows wait for their peers' flag-tile bits (relaxed polls, one
-//    acquire), then add the peers in ascending rank order (fp32) and store to
-//    `out`; other rows are converted and stored to `send`.  No per-tile drain
-//    on `out` (the kernel end is its release); a drain + balanced barrier +
-//    one release precede the ready_out bits of `send` tiles.
+//  * Workgroup tile BM x BN of 4 or 8 waves, each wave a WM x WN block of
+//    32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulators).  The
+//    8-wave 256x256 tile runs two waves per SIMD: one wave issues MFMAs while
+//    the other waits on its loads.
+//  * K is walked in BK-wide steps through an S-stage LDS ring filled by
+//    direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds, issued as inline
+//    asm so the compiler adds no waits of its own); a stage is read only after
+//    an exact vmcnt wait and a barrier.  Out-of-range offsets zero-fill the
+//    M, N and K tails.  With S >= 3 a step's loads are spread between its MFMA
+//    groups instead of being issued as one burst.
+//  * X [M,K] is K-contiguous in LDS and read with 16-byte swizzled reads.  W
+//    [K,N] stays N-contiguous in LDS and is read with the gfx950 transpose
+//    read (ds_read_b64_tr_b16), which yields the B-operand layout directly.
+//    MFMAs and operand reads of the next sub-step are interleaved with
+//    scheduling groups.
+//  * Rows: a row block is two half-blocks (chunks) of BM/2 rows, interleaved
+//    between the wave rows.  Optionally (AREPI_TILE_PAIRED_ROWS) an owner
+//    half-block is paired with a non-owner one.
+//  * Epilogue, chosen per workgroup at entry (no-owner / owner-chunk-A /
+//    owner-rows-anywhere bodies): accumulators go through LDS one 32-row slab
+//    at a time and come back row-contiguous; owner rows wait for their peers'
+//    flag-tile bits (one lane per (peer, tile), relaxed polls, one acquire),
+//    add the peers' packs (fetched several units ahead with row-coalesced
+//    loads, ascending rank order, fp32) and store to `out`; other rows are
+//    stored to `send`.  Stores are buffer stores whose out-of-range offsets
+//    drop lanes, so the code has no data-dependent branches around memory
+//    operations.  No per-tile drain on `out` (the kernel end is its release);
+//    a drain + balanced barrier + one release precede the ready_out bits.
 //  * Tile order: row blocks rotated so the owner segment comes last (the
 //    destination-rotated order of the mori page's tile-order commit), grouped
 //    G row blocks at a time, and remapped so that the blocks one XCD runs
@@ -42,7 +49,6 @@
 namespace arepi {
 namespace {
 
-constexpr int BK = 64;
 constexpr int kMaxR = 8;
 constexpr int kXcds = 8;
 
@@ -183,7 +189,7 @@ constexpr int lds_bytes() { return S * (BM * BK * 2 + BK * BN * 2); }
 // all of them through vector registers).
 enum { kNoOwnerRows = 0, kOwnerChunkA = 1, kOwnerRowsAnywhere = 2 };
 
-template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, int KIND, bool WT>
+template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, int KIND>
 __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *smem, int rb, int cb, int64_t a0,
                                              int alen, int64_t b0, int blen) {
     constexpr int NWN = BN / WN;
@@ -205,7 +211,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     static_assert(CH == 4 || CH == 8, "BK must be 32 or 64");
     static_assert(A_INSTR >= 1 && A_INSTR * NW * 1024 == A_BYTES, "X stage split");
     static_assert(B_INSTR >= 1 && B_INSTR * NW * 1024 == B_BYTES, "W stage split");
-    static_assert(WT || (B_CPR >= 16 && B_CPR <= 64), "W swizzle needs 16..64 chunks per row");
+    static_assert(B_CPR >= 16 && B_CPR <= 64, "W swizzle needs 16..64 chunks per row");
     static_assert(NW * ER * EPS * 4 <= LDS_BYTES, "epilogue slabs must fit the stage memory");
     static_assert(S >= 2 && (S - 2) * NDMA < 64, "stage count vs vmcnt range");
 
@@ -244,9 +250,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     // or N get an out-of-range offset); k0 goes into the scalar offset.
     auto a_row_of = [&](int i) { return (wave * A_INSTR + i) * A_RPI + lane / CH; };
     auto a_col_of = [&](int i) { return ((lane % CH) ^ swz_a<CH>(a_row_of(i))) * 8; };
-    // (W stored as [N,K] (WT): its tile is K-contiguous like X's, same layout and swizzle)
-    auto b_row_of = [&](int i) { return WT ? (wave * B_INSTR + i) * A_RPI + lane / CH : (wave * B_INSTR + i) * B_RPI + lane / B_CPR; };
-    auto b_col_of = [&](int i) { return ((lane % CH) ^ swz_a<CH>(b_row_of(i))) * 8; };  // WT only
+    auto b_row_of = [&](int i) { return (wave * B_INSTR + i) * B_RPI + lane / B_CPR; };
     uint32_t a_off[A_INSTR], b_off[B_INSTR];
 #pragma unroll
     for (int i = 0; i < A_INSTR; ++i) {
@@ -255,19 +259,12 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     }
 #pragma unroll
     for (int i = 0; i < B_INSTR; ++i) {
-        if constexpr (WT) {
-            const int64_t gn = n0 + b_row_of(i);
-            b_off[i] = (gn < N) ? (uint32_t)((gn * K + b_col_of(i)) * 2) : kOob;
-        } else {
-            const int r = b_row_of(i);
-            const int64_t gn = n0 + ((lane % B_CPR) ^ swz_b(r)) * 8;
-            b_off[i] = (gn < N) ? (uint32_t)((r * N + gn) * 2) : kOob;
-        }
+        const int r = b_row_of(i);
+        const int64_t gn = n0 + ((lane % B_CPR) ^ swz_b(r)) * 8;
+        b_off[i] = (gn < N) ? (uint32_t)((r * N + gn) * 2) : kOob;
     }
-    // byte step of W per k (soffset per K step) and whether lane's W k is in range
-    constexpr int64_t one = 1;
-    const int64_t w_kstride = WT ? 2 * one : N * 2;
-    auto b_k_of = [&](int i) { return WT ? b_col_of(i) : b_row_of(i); };
+    const int64_t w_kstride = N * 2;  // bytes of W per k
+    auto b_k_of = [&](int i) { return b_row_of(i); };
 
     lds_t *const S0 = (lds_t *)smem;
     auto lds_addr = [](const lds_t *ptr) { return (uint32_t)(uintptr_t)ptr; };
@@ -361,12 +358,6 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            if constexpr (WT) {
-                const int r = wn * WN + j * 32 + (lane & 31);
-                const int c = kk * 2 + (lane >> 5);
-                f.b[j] = *(const __attribute__((address_space(3))) bf16x8 *)(Bs + r * (BK * 2) + ((c ^ swz_a<CH>(r)) << 4));
-                continue;
-            }
             const int n = wn * WN + j * 32 + b_n_lane;
             bf16x4 h[2];
 #pragma unroll
@@ -392,12 +383,6 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             if ((j * TM) / TN != pc) continue;
-            if constexpr (WT) {
-                const int r = wn * WN + j * 32 + (lane & 31);
-                const int c = kk * 2 + (lane >> 5);
-                f.b[j] = *(const __attribute__((address_space(3))) bf16x8 *)(Bs + r * (BK * 2) + ((c ^ swz_a<CH>(r)) << 4));
-                continue;
-            }
             const int n = wn * WN + j * 32 + b_n_lane;
             bf16x4 h[2];
 #pragma unroll
@@ -412,7 +397,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     };
     auto reads_in_piece = [](int pc) {
         int n = 1;
-        for (int j = 0; j < TN; ++j) n += ((j * TM) / TN == pc) ? (WT ? 1 : 2) : 0;
+        for (int j = 0; j < TN; ++j) n += ((j * TM) / TN == pc) ? 2 : 0;
         return n;
     };
     auto mma_row = [&](const Frag &f, int i) {
@@ -430,14 +415,12 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     // Scheduling groups: after each MFMA one LDS operand read, so the reads of
     // the next sub-step overlap the MFMAs of the current one (the compiler's
     // default is to drain each read right before its first use).
-    constexpr int NREAD = TM + (WT ? 1 : 2) * TN;  // LDS reads per sub-step
+    constexpr int NREAD = TM + 2 * TN;  // LDS reads per sub-step
     constexpr int NMMA = TM * TN;       // MFMAs per sub-step
     constexpr int NK = BK / 16;         // MFMA sub-steps per K step
     static_assert(NK % 2 == 0, "sub-step parity must repeat across K steps");
-#ifndef AREPI_SPREAD_LOADS
-#define AREPI_SPREAD_LOADS 1
-#endif
-    constexpr bool kSpreadLoads = AREPI_SPREAD_LOADS != 0 && S >= 3;
+    // the S >= 3 rings issue a step's loads spread through the step
+    constexpr bool kSpreadLoads = S >= 3;
     constexpr int kHalf = (NDMA + 1) / 2;  // loads of a step issued before its stage barrier
     auto interleave = [&]() {
 #pragma unroll
@@ -787,7 +770,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
 
 // WPE: waves per SIMD the register allocation targets (1 = one big-tile
 // workgroup per CU; 2 = two co-resident workgroups; 0 = no target).
-template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, bool WT>
+template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, WPE > 0 ? WPE : 8)))
     gemm_rs_kernel(const GemmRsParams p) {
@@ -802,11 +785,11 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     const bool own_a = alen > 0 && a0 < oseg1 && a0 + alen > oseg0;
     const bool own_b = blen > 0 && b0 < oseg1 && b0 + blen > oseg0;
     if (!own_a && !own_b)
-        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kNoOwnerRows, WT>(p, smem, rb, cb, a0, alen, b0, blen);
+        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kNoOwnerRows>(p, smem, rb, cb, a0, alen, b0, blen);
     else if (p.paired)  // paired half-blocks: only chunk A can be an owner chunk
-        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerChunkA, WT>(p, smem, rb, cb, a0, alen, b0, blen);
+        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerChunkA>(p, smem, rb, cb, a0, alen, b0, blen);
     else
-        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerRowsAnywhere, WT>(p, smem, rb, cb, a0, alen, b0, blen);
+        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerRowsAnywhere>(p, smem, rb, cb, a0, alen, b0, blen);
 }
 
 // ---- host side --------------------------------------------------------------------
@@ -943,19 +926,15 @@ int plan(GemmRsParams &p, const TileCfg *t, int64_t M, int64_t N, int64_t K, int
     return AREPI_OK;
 }
 
-#ifndef AREPI_EXP_WT
-#define AREPI_EXP_WT 0
-#endif
 template <int BM, int BN, int WM, int WN, int BK, int S, int WPE>
 void launch(const GemmRsParams &p, hipStream_t stream) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
-    constexpr bool WT = AREPI_EXP_WT != 0;
     if (p.npeers <= 1)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1, WT>), dim3(p.nWG), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1>), dim3(p.nWG), dim3(NT), 0, stream, p);
     else if (p.npeers <= 3)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3, WT>), dim3(p.nWG), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3>), dim3(p.nWG), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1, WT>), dim3(p.nWG), dim3(NT), 0,
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1>), dim3(p.nWG), dim3(NT), 0,
                            stream, p);
 }
 

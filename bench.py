@@ -33,20 +33,74 @@ LAMPORT_BYTES_NO_REARM = 528_482_304 + 7168 * 2
 COMBINE_BYTES = 528_613_376              # read x + gate + write out
 
 
+class _HipEvents:
+    """HIP events created with flags torch does not expose: timing events
+    without the system-scope fence an event record performs by default, and an
+    ordering event with a device-scope release (enough for work that stays on
+    this GPU).  Each default record costs several microseconds of cache
+    writeback and invalidation and would sit on the measured path."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, flags):
+        e = self.ct.c_void_p()
+        if self.lib.hipEventCreateWithFlags(self.ct.byref(e), flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return e
+
+    def record(self, e, stream):
+        if self.lib.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def wait(self, stream, e):
+        if self.lib.hipStreamWaitEvent(self.ct.c_void_p(stream.cuda_stream), e, 0) != 0:
+            raise RuntimeError("hipStreamWaitEvent failed")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.lib.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, events):
+        for e in events:
+            self.lib.hipEventDestroy(e)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sweep", action="store_true", help="also time the tp=8 sweep and the pre-staged tp=4 kernel")
-    ap.add_argument("--only", default=None, choices=[None, "gemm_rs", "lamport", "combine"],
-                    help="run a single path (used for per-kernel profiles)")
+    ap.add_argument("--only", default=None, choices=[None, "gemm_rs", "gemm_rs_prestaged", "lamport", "combine"],
+                    help="run a single path (used for per-kernel profiles; counter collection serializes "
+                         "kernels, so the GEMM's counters are taken pre-staged, without the producer stream)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     return ap.parse_args()
 
 
 def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
-    """tp=4 share; producer stream lands the peers while the GEMM runs."""
+    """tp=4 share; a producer stream lands the peers while the GEMM runs.
+
+    Each step: clear ready_in on the main stream (after the previous GEMM, which
+    could only finish once every bit of the previous producer had landed), then
+    the GEMM on the main stream and the producer on the side stream run
+    concurrently; the GEMM's owner tiles wait for the producer's bits.
+    ready_out is only ever OR-ed into, so it needs no clearing.  The producer's
+    waves share CUs with the GEMM's (the chosen tile leaves registers for them).
+    """
     dev = torch.device("cuda:0")
     case = inputs.workload_gemm_rs(2)
     M, N, K, R, owner = case["M"], case["N"], case["K"], case["R"], case["owner"]
@@ -70,26 +124,20 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
     side = torch.cuda.Stream()
     tile = A.gemm_rs_pick_tile(M, N, K, R, owner, publish=True)
     n_ev = steps + warmup
-    ev_gs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev_ge = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev_clear = [torch.cuda.Event() for _ in range(n_ev)]
+    H = _HipEvents()
+    ev_gs = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n_ev)]
+    ev_ge = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n_ev)]
+    ev_clear = [H.create(H.RELEASE_TO_DEVICE | 0x2) for _ in range(n_ev)]  # 0x2: no timing
 
     def step(i):
-        # Each step: clear ready_in on the main stream (after the previous GEMM,
-        # which could only finish once every bit of the previous producer had
-        # landed), then the GEMM on the main stream and the producer on the side
-        # stream run concurrently; the GEMM's owner tiles wait for the
-        # producer's bits.  ready_out is only ever OR-ed into: no clearing.
-        # (The producer's waves share CUs with the GEMM's: the chosen tile
-        # leaves the registers for them.)
         rin.zero_()
-        ev_clear[i].record(main)
-        side.wait_event(ev_clear[i])
+        H.record(ev_clear[i], main)
+        H.wait(side, ev_clear[i])
         A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, owner, M, N, stream=side)
-        ev_gs[i].record(main)
+        H.record(ev_gs[i], main)
         A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile,
                         status=status, stream=main)
-        ev_ge[i].record(main)
+        H.record(ev_ge[i], main)
 
     for i in range(warmup):
         step(i)
@@ -99,7 +147,8 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
         step(i)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    gemm_ms = sum(ev_gs[i].elapsed_time(ev_ge[i]) for i in range(warmup, warmup + steps)) / steps
+    gemm_ms = sum(H.elapsed_ms(ev_gs[i], ev_ge[i]) for i in range(warmup, warmup + steps)) / steps
+    H.destroy(ev_gs + ev_ge + ev_clear)
     if int(status.item()) != 0:
         raise RuntimeError("a readiness wait timed out during the benchmark")
     flops = 2.0 * M * N * K
@@ -270,7 +319,7 @@ def main():
         secondary["lamport_ar_rmsnorm"] = lamport(A, inputs, torch, max(10, a.steps // 2), 3)
     if a.only in (None, "combine"):
         secondary["combine_reduce"] = combine(A, inputs, torch, max(10, a.steps // 2), 3)
-    if a.only in (None, "gemm_rs"):
+    if a.only in (None, "gemm_rs", "gemm_rs_prestaged"):
         secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2)
     if a.sweep:
         secondary["gemm_rs_tp8_sweep"] = [gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 3, M=m)
