@@ -27,6 +27,7 @@ STATUS_TIMEOUT = 1
 (TILE_AUTO, TILE_256x256, TILE_128x256, TILE_128x128, TILE_64x128, TILE_32x256, TILE_256x256_S4,
  TILE_256x128_S3, TILE_128x256_S3, TILE_128x128_S4, TILE_256x256_W8) = range(11)
 TILE_PAIRED_ROWS = 0x200  # OR into an explicit tile: pair owner half-blocks with non-owner ones
+TILE_CONSUME_READY = 0x400  # OR into any tile: owner tiles clear the ready_in bits they waited for
 TILE_NAMES = {TILE_256x256: "256x256", TILE_128x256: "128x256", TILE_128x128: "128x128",
               TILE_64x128: "64x128", TILE_32x256: "32x256", TILE_256x256_S4: "256x256_s4",
               TILE_256x128_S3: "256x128_s3", TILE_128x256_S3: "128x256_s3", TILE_128x128_S4: "128x128_s4", TILE_256x256_W8: "256x256_w8"}
@@ -71,7 +72,7 @@ def lib():
             "arepi_ar_rmsnorm_lamport": ([vp, vp, vp, i64, i64, i32, f32, i32, u32p, i64, vp], i32),
             "arepi_combine_reduce": ([vp, vp, vp, i64, i32, i64, vp], i32),
             "arepi_combine_reduce_lds": ([vp, vp, vp, i64, i32, i64, vp], i32),
-            "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp], i32),
+            "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -203,8 +204,10 @@ def gemm_rs_fused(x, w, recv, ready_in, out, R: int, owner: int, send=None, read
 
 
 def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N: int,
-                      flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT, stream=None):
-    """Test-only: land (peer, tile) items of src[p] into recv[p] and set their bits."""
+                      flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT,
+                      workgroups: int = 0, stream=None):
+    """Test-only: land (peer, tile) items of src[p] into recv[p] and set their bits
+    (workgroups > 0: that many items in flight at a time)."""
     seg = M // R
     torch = _torch()
     _need(order, "order", (torch.int32,))
@@ -223,7 +226,7 @@ def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N:
         rp[p] = recv[p].data_ptr()
     rc = lib().arepi_emu_peer_producer(ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p),
                                        _ptr(ready_in), _ptr(order), order.shape[0], M, N, R, owner,
-                                       flag_tile_m, flag_tile_n, scope, _stream(stream))
+                                       flag_tile_m, flag_tile_n, scope, workgroups, _stream(stream))
     _check(rc, "emu_peer_producer")
 
 

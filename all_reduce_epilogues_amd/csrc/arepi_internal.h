@@ -88,6 +88,12 @@ __device__ __forceinline__ void fetch_or_relaxed(uint32_t *p, uint32_t v, bool s
     else
         __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void fetch_and_relaxed(uint32_t *p, uint32_t v, bool system) {
+    if (system)
+        __hip_atomic_fetch_and(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    else
+        __hip_atomic_fetch_and(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void fence_acquire(bool system) {
     if (system)
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");

@@ -4,6 +4,7 @@
 // workgroup barrier, and one thread publishes the tile's bit with a release --
 // the per-tile readiness of DeepGEMM PR #1 "Fused ring RS: per-tile bitmask",
 // in the place of a per-segment flag.
+#include <algorithm>
 #include <string>
 
 #include "arepi_internal.h"
@@ -18,14 +19,14 @@ struct EmuParams {
     uint16_t *recv[kMaxR];
     uint32_t *ready_in;
     const int32_t *order;  // [n_items][2] = (peer, tile)
-    int64_t seg, N, ftiles_n, ftiles, fwords;
+    int64_t n_items, seg, N, ftiles_n, ftiles, fwords;
     int ftm, ftn, R, owner, system_scope;
 };
 
-__global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
-    // one workgroup of 256 threads per (peer, flag tile) item
-    const int peer = p.order[2 * (int64_t)blockIdx.x];
-    const int64_t t = p.order[2 * (int64_t)blockIdx.x + 1];
+// Lands one (peer, flag tile) item with the whole workgroup.
+__device__ void land_item(const EmuParams &p, const int64_t item) {
+    const int peer = p.order[2 * item];
+    const int64_t t = p.order[2 * item + 1];
     const bool valid = peer >= 0 && peer < p.R && peer != p.owner && t >= 0 && t < p.ftiles;
     if (!valid) return;  // uniform across the workgroup
     const int64_t r0 = (t / p.ftiles_n) * p.ftm, c0 = (t % p.ftiles_n) * p.ftn;
@@ -39,20 +40,31 @@ __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
             s = p.src[i];
             d = p.recv[i];
         }
-    // 16-byte packs, eight per thread in flight (streaming loads and stores)
+    // 16-byte packs, eight per thread in flight (streaming loads and stores).
+    // Whole rounds of 256 x 8 packs run without per-pack predicates: a store
+    // under a branch would make the compiler wait for every load in flight.
     const int ppr = (int)packs, total = (int)rows * ppr;
-    for (int base = 0; base < total; base += 256 * 8) {
+    auto at = [&](int i) { return (r0 + i / ppr) * p.N + c0 + (i % ppr) * 8; };
+    int base = 0;
+    for (; base + 256 * 8 <= total; base += 256 * 8) {
         uint4 v[8];
-        int64_t off[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = load16_nt(s + at(base + (int)threadIdx.x + k * 256));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) store16_nt(d + at(base + (int)threadIdx.x + k * 256), v[k]);
+    }
+    if (base < total) {
+        uint4 v[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int i = base + (int)threadIdx.x + k * 256;
-            off[k] = i < total ? (r0 + i / ppr) * p.N + c0 + (i % ppr) * 8 : -1;
-            if (off[k] >= 0) v[k] = load16_nt(s + off[k]);
+            if (i < total) v[k] = load16_nt(s + at(i));
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (off[k] >= 0) store16_nt(d + off[k], v[k]);
+        for (int k = 0; k < 8; ++k) {
+            const int i = base + (int)threadIdx.x + k * 256;
+            if (i < total) store16_nt(d + at(i), v[k]);
+        }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -63,6 +75,12 @@ __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
     }
 }
 
+// Workgroup g lands items g, g + G, g + 2G, ... (G = grid size), so a grid
+// smaller than the item count paces the landing like a link of bounded rate.
+__global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
+    for (int64_t item = blockIdx.x; item < p.n_items; item += gridDim.x) land_item(p, item);
+}
+
 }  // namespace
 }  // namespace arepi
 
@@ -71,7 +89,7 @@ using namespace arepi;
 extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
                                        const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
                                        int owner, int flag_tile_m, int flag_tile_n, int scope,
-                                       arepi_stream_t stream) {
+                                       int workgroups, arepi_stream_t stream) {
     auto bad = [](const std::string &m) { return fail(AREPI_EINVAL, "arepi_emu_peer_producer: " + m); };
     if (R < 1 || R > kMaxR) return bad("R=" + std::to_string(R) + " outside [1, 8]");
     if (owner < 0 || owner >= R) return bad("owner outside [0, R-1]");
@@ -81,6 +99,7 @@ extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *con
         return bad("flag tile needs flag_tile_m >= 1 and flag_tile_n a positive multiple of 8");
     if (scope != AREPI_SCOPE_AGENT && scope != AREPI_SCOPE_SYSTEM) return bad("scope must be AGENT or SYSTEM");
     if (n_items < 0 || n_items > (int64_t)1 << 30) return bad("n_items out of range");
+    if (workgroups < 0) return bad("workgroups must be >= 0 (0: one per item)");
     if (n_items == 0) return ok();
     if (!src || !recv || !ready_in || !order) return bad("src, recv, ready_in and order must be non-NULL");
     EmuParams p{};
@@ -93,6 +112,7 @@ extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *con
     }
     p.ready_in = ready_in;
     p.order = order;
+    p.n_items = n_items;
     p.seg = M / R;
     p.N = N;
     p.ftiles_n = (N + flag_tile_n - 1) / flag_tile_n;
@@ -103,7 +123,8 @@ extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *con
     p.R = R;
     p.owner = owner;
     p.system_scope = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
-    hipLaunchKernelGGL(emu_producer_kernel, dim3((unsigned)n_items), dim3(256), 0,
+    const int64_t groups = workgroups == 0 ? n_items : std::min<int64_t>(workgroups, n_items);
+    hipLaunchKernelGGL(emu_producer_kernel, dim3((unsigned)groups), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), p);
     return check_launch("arepi_emu_peer_producer");
 }

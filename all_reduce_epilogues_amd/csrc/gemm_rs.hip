@@ -57,7 +57,7 @@ struct GemmRsParams {
     const uint16_t *w;
     const uint16_t *peer[kMaxR - 1];  // peer partials in ascending rank order, owner skipped
     int npeers;                       // R - 1
-    const uint32_t *ready_in;
+    uint32_t *ready_in;
     uint16_t *out;
     uint16_t *send;
     uint32_t *ready_out;
@@ -76,6 +76,7 @@ struct GemmRsParams {
     // with a non-owner chunk, so the owner rows' peer reads are spread over nc
     // row blocks instead of seg/BM.
     int paired, nc, npure, nleft;
+    int consume;  // owner tiles clear the ready_in bits they waited for
 };
 
 // gfx9 buffer-resource word 3 (raw, untyped 32-bit data format).
@@ -538,16 +539,22 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                 th[h] = ((lr1 - 1) / p.ftm - tr0[h] + 1) * ntc;
             }
             const int per_peer = th[0] + th[1], items = p.npeers * per_peer;
-            int64_t spins = 0;
-            for (int k = lane; k < items; k += 64) {
+            // word and bit of item k
+            auto item = [&](int k, uint32_t *&word, uint32_t &bit) {
                 const int slot = k / per_peer;
                 int ti = k % per_peer;
                 const int h = ti < th[0] ? 0 : 1;
                 ti -= h ? th[0] : 0;
                 const int t = ((h ? tr0[1] : tr0[0]) + ti / ntc) * (int)p.ftiles_n + tc0 + ti % ntc;
                 const int rank = slot < p.owner ? slot : slot + 1;
-                const uint32_t *word = p.ready_in + (int64_t)rank * p.fwords + (t >> 5);
-                while (!(load_relaxed(word, sys) & (1u << (t & 31)))) {
+                word = p.ready_in + (int64_t)rank * p.fwords + (t >> 5);
+                bit = 1u << (t & 31);
+            };
+            int64_t spins = 0;
+            for (int k = lane; k < items; k += 64) {
+                uint32_t *word, bit;
+                item(k, word, bit);
+                while (!(load_relaxed(word, sys) & bit)) {
                     if (++spins > p.spin_limit) {
                         if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
                         break;
@@ -555,6 +562,16 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                     __builtin_amdgcn_s_sleep(2);
                 }
             }
+            // Each flag tile lies under exactly one workgroup's rows and
+            // columns (checked on the host), so no other workgroup waits for
+            // the bits cleared here; the kernel's end makes the clears visible
+            // to whatever the stream runs next.
+            if (p.consume)
+                for (int k = lane; k < items; k += 64) {
+                    uint32_t *word, bit;
+                    item(k, word, bit);
+                    fetch_and_relaxed(word, ~bit, sys);
+                }
             fence_acquire(sys);
         }
         __syncthreads();
@@ -969,15 +986,18 @@ extern "C" int arepi_gemm_rs_supports(int64_t M, int64_t N, int64_t K, int R, in
                                       int flag_tile_m, int flag_tile_n, int publish, int tile_cfg) {
     int rc = validate_shape(M, N, K, R, owner, flag_tile_m, flag_tile_n);
     if (rc) return rc;
-    if (tile_cfg == AREPI_TILE_AUTO) {
-        rc = arepi_gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish);
+    const bool consume = (tile_cfg & AREPI_TILE_CONSUME_READY) != 0;
+    // consuming readiness bits needs the same nesting as publishing them
+    const bool nest = publish || consume;
+    if ((tile_cfg & ~AREPI_TILE_CONSUME_READY) == AREPI_TILE_AUTO) {
+        rc = arepi_gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m, flag_tile_n, nest);
         return rc < 0 ? rc : ok();
     }
     const bool contiguous = (tile_cfg & AREPI_TILE_PAIRED_ROWS) == 0;
-    const int id = tile_cfg & ~AREPI_TILE_PAIRED_ROWS;
+    const int id = tile_cfg & ~(AREPI_TILE_PAIRED_ROWS | AREPI_TILE_CONSUME_READY);
     const TileCfg *t = id == AREPI_TILE_AUTO ? nullptr : find_tile(id);
     if (!t) return fail(AREPI_EINVAL, "arepi_gemm_rs: tile_cfg=" + std::to_string(tile_cfg) + " is not an AREPI_TILE_* value");
-    if (publish && !flags_nest(M, N, R, flag_tile_m, flag_tile_n, t->BM, t->BN) &&
+    if (nest && !flags_nest(M, N, R, flag_tile_m, flag_tile_n, t->BM, t->BN) &&
         !use_paired(M, N, R, flag_tile_m, flag_tile_n, t->BM, t->BN, true, contiguous))
         return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: flag tiles " + std::to_string(flag_tile_m) + "x" +
                                             std::to_string(flag_tile_n) + " straddle " + std::to_string(t->BM) +
@@ -985,8 +1005,25 @@ extern "C" int arepi_gemm_rs_supports(int64_t M, int64_t N, int64_t K, int R, in
     return ok();
 }
 
+// Tile id, row layout and options of a validated tile_cfg.
+struct CfgChoice {
+    const TileCfg *t;
+    int id;
+    bool contiguous, consume, nest;
+};
+static CfgChoice decode_cfg(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool publish, int tile_cfg) {
+    CfgChoice c{};
+    c.consume = (tile_cfg & AREPI_TILE_CONSUME_READY) != 0;
+    c.nest = publish || c.consume;
+    c.contiguous = (tile_cfg & AREPI_TILE_PAIRED_ROWS) == 0;
+    const int id = tile_cfg & ~(AREPI_TILE_PAIRED_ROWS | AREPI_TILE_CONSUME_READY);
+    c.id = id == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, ftm, ftn, c.nest) : id;
+    c.t = find_tile(c.id);
+    return c;
+}
+
 extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const uint16_t *const *recv,
-                                   const uint32_t *ready_in, uint16_t *out, uint16_t *send,
+                                   uint32_t *ready_in, uint16_t *out, uint16_t *send,
                                    uint32_t *ready_out, int64_t M, int64_t N, int64_t K, int R, int owner,
                                    int flag_tile_m, int flag_tile_n, int scope, int tile_cfg,
                                    uint32_t *status, int64_t spin_limit, arepi_stream_t stream) {
@@ -1009,10 +1046,8 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
             if (!aligned16(recv[p])) return bad("recv[" + std::to_string(p) + "] must be 16-byte aligned");
         }
     }
-    const bool contiguous = (tile_cfg & AREPI_TILE_PAIRED_ROWS) == 0;
-    const int cfg = tile_cfg == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, flag_tile_m, flag_tile_n, publish)
-                                                : tile_cfg & ~AREPI_TILE_PAIRED_ROWS;
-    const TileCfg *t = find_tile(cfg);
+    const CfgChoice c = decode_cfg(M, N, K, R, flag_tile_m, flag_tile_n, publish, tile_cfg);
+    const int cfg = c.id;
 
     GemmRsParams p{};
     p.x = x;
@@ -1027,7 +1062,8 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
     p.status = status;
     p.spin_limit = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
     p.system_scope = scope == AREPI_SCOPE_SYSTEM;
-    rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, publish, contiguous);
+    p.consume = c.consume ? 1 : 0;
+    rc = plan(p, c.t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous);
     if (rc) return rc;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -1052,12 +1088,10 @@ extern "C" int64_t arepi_gemm_rs_schedule(int64_t M, int64_t N, int64_t K, int R
                                           int64_t capacity) {
     int rc = arepi_gemm_rs_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish, tile_cfg);
     if (rc) return rc;
-    const bool contiguous = (tile_cfg & AREPI_TILE_PAIRED_ROWS) == 0;
-    const int cfg = tile_cfg == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, flag_tile_m, flag_tile_n, publish != 0)
-                                                : tile_cfg & ~AREPI_TILE_PAIRED_ROWS;
-    const TileCfg *t = find_tile(cfg);
+    const CfgChoice c = decode_cfg(M, N, K, R, flag_tile_m, flag_tile_n, publish != 0, tile_cfg);
+    const TileCfg *t = c.t;
     GemmRsParams p{};
-    rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, publish != 0, contiguous);
+    rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous);
     if (rc) return rc;
     if (rows) {
         if (capacity < (int64_t)p.nWG * 6)

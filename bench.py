@@ -34,14 +34,13 @@ COMBINE_BYTES = 528_613_376              # read x + gate + write out
 
 
 class _HipEvents:
-    """HIP events created with flags torch does not expose: timing events
-    without the system-scope fence an event record performs by default, and an
-    ordering event with a device-scope release (enough for work that stays on
-    this GPU).  Each default record costs several microseconds of cache
-    writeback and invalidation and would sit on the measured path."""
+    """HIP events created with a flag torch does not expose: no system-scope
+    fence when the record completes.  A default record costs several
+    microseconds of cache writeback and invalidation on the measured path; the
+    work these events order stays on this GPU, and each kernel already ends
+    with a device-scope release of its own writes."""
 
     DISABLE_SYSTEM_FENCE = 0x20000000
-    RELEASE_TO_DEVICE = 0x40000000
 
     def __init__(self):
         import ctypes
@@ -94,12 +93,16 @@ def parse():
 def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
     """tp=4 share; a producer stream lands the peers while the GEMM runs.
 
-    Each step: clear ready_in on the main stream (after the previous GEMM, which
-    could only finish once every bit of the previous producer had landed), then
-    the GEMM on the main stream and the producer on the side stream run
-    concurrently; the GEMM's owner tiles wait for the producer's bits.
-    ready_out is only ever OR-ed into, so it needs no clearing.  The producer's
-    waves share CUs with the GEMM's (the chosen tile leaves registers for them).
+    The main stream runs only the GEMMs, back to back.  Each consumes its
+    ready_in bits (the owner tiles clear what they waited for), so ready_in is
+    zero again when it ends and needs no clearing kernel.  The producer of step
+    i, on the side stream, waits for GEMM i-1 to end (it reuses recv and
+    ready_in) and then runs while GEMM i does; GEMM i's owner tiles wait for
+    its bits.  ready_out is only ever OR-ed into.  The producer's waves share
+    CUs with the GEMM's (the chosen tile leaves registers for them).
+
+    Returns the wall time per step and the GEMM's average launch duration from
+    HIP events recorded on its stream just before and after each launch.
     """
     dev = torch.device("cuda:0")
     case = inputs.workload_gemm_rs(2)
@@ -127,16 +130,14 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
     H = _HipEvents()
     ev_gs = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n_ev)]
     ev_ge = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n_ev)]
-    ev_clear = [H.create(H.RELEASE_TO_DEVICE | 0x2) for _ in range(n_ev)]  # 0x2: no timing
 
     def step(i):
-        rin.zero_()
-        H.record(ev_clear[i], main)
-        H.wait(side, ev_clear[i])
+        if i > 0:
+            H.wait(side, ev_ge[i - 1])
         A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, owner, M, N, stream=side)
         H.record(ev_gs[i], main)
-        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile,
-                        status=status, stream=main)
+        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout,
+                        tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
         H.record(ev_ge[i], main)
 
     for i in range(warmup):
@@ -148,7 +149,7 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     gemm_ms = sum(H.elapsed_ms(ev_gs[i], ev_ge[i]) for i in range(warmup, warmup + steps)) / steps
-    H.destroy(ev_gs + ev_ge + ev_clear)
+    H.destroy(ev_gs + ev_ge)
     if int(status.item()) != 0:
         raise RuntimeError("a readiness wait timed out during the benchmark")
     flops = 2.0 * M * N * K

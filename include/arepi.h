@@ -75,7 +75,12 @@ enum {
      * which spreads the owner rows' peer reads over twice as many workgroups.
      * Without it (and for other shapes) each workgroup's rows are one
      * contiguous block. */
-    AREPI_TILE_PAIRED_ROWS = 0x200
+    AREPI_TILE_PAIRED_ROWS = 0x200,
+    /* ORed into any tile_cfg (AUTO included): the owner tiles clear each
+     * ready_in bit they waited for, so ready_in is all zero again when the
+     * call ends and the next call can use it without a separate clear.  Needs
+     * the flag tiles to nest inside the compute tiles, as ready_out does. */
+    AREPI_TILE_CONSUME_READY = 0x400
 };
 
 /* Message describing the last failed call on this thread ("" if none). */
@@ -99,7 +104,9 @@ const char *arepi_version(void);
  *   recv     HOST array of R device pointers; recv[p] is bf16 [M/R,N], peer p's
  *            partial of this rank's owner segment; recv[owner] is ignored.
  *   ready_in u32 [R][words]; bit t (word t/32, bit t%32) of peer p says flag
- *            tile t of recv[p] has landed.  Read-only.  Flag tiles are
+ *            tile t of recv[p] has landed.  Read-only, unless tile_cfg has
+ *            AREPI_TILE_CONSUME_READY (then the owner-segment bits this call
+ *            waited for are cleared before it ends).  Flag tiles are
  *            flag_tile_m x flag_tile_n pieces of a segment, clipped at its
  *            edges, numbered row-major; words = arepi_gemm_rs_flag_words().
  *   out      bf16 [M/R,N]: out[i,n] = bf16(C[owner*M/R + i, n] + sum over
@@ -137,7 +144,7 @@ int64_t arepi_gemm_rs_schedule(int64_t M, int64_t N, int64_t K, int R, int owner
                                int64_t capacity);
 
 int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const uint16_t *const *recv,
-                        const uint32_t *ready_in, uint16_t *out, uint16_t *send,
+                        uint32_t *ready_in, uint16_t *out, uint16_t *send,
                         uint32_t *ready_out, int64_t M, int64_t N, int64_t K, int R, int owner,
                         int flag_tile_m, int flag_tile_n, int scope, int tile_cfg,
                         uint32_t *status, int64_t spin_limit, arepi_stream_t stream);
@@ -205,10 +212,14 @@ int arepi_combine_reduce_lds(const uint16_t *x, const float *gate, uint16_t *out
  * t): copy flag tile t of src[p] (bf16 [M/R,N]) into recv[p], then set bit t
  * of ready_in[p] with a release at `scope`.  src and recv are HOST arrays of R
  * device pointers (entry `owner` ignored); ready_in must be zero beforehand.
+ * workgroups = 0 lands every item at once (one workgroup each); workgroups =
+ * G > 0 lands them G at a time, in order, which paces the arrivals like a link
+ * of bounded rate and leaves the other compute units to the consumer.
+ * Errors: EINVAL for bad shapes, NULL pointers or workgroups < 0.
  * ------------------------------------------------------------------------ */
 int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
                             const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
-                            int owner, int flag_tile_m, int flag_tile_n, int scope,
+                            int owner, int flag_tile_m, int flag_tile_n, int scope, int workgroups,
                             arepi_stream_t stream);
 
 #ifdef __cplusplus

@@ -74,6 +74,9 @@ def test_supports_matches_flag_nesting(M, N, R, ftm, ftn):
         assert (rc == 0) == expect, (tile, A.last_error())
         # without publication every tile is allowed
         assert A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=False, tile=tile) == 0
+        # consuming ready_in bits needs the same nesting as publishing
+        rc = A.gemm_rs_supports(M, N, 64, R, 0, ftm, ftn, publish=False, tile=tile | A.TILE_CONSUME_READY)
+        assert (rc == 0) == nests(M, N, R, ftm, ftn, BM, BN), (tile, A.last_error())
 
 
 def paired_eligible(M, R, BM):
@@ -199,7 +202,7 @@ def test_lamport_and_combine_validate_before_launch():
     assert L.arepi_combine_reduce(None, None, None, 4, 8, 60, None) == A.EINVAL
     assert L.arepi_combine_reduce(None, None, None, 0, 8, 64, None) == A.OK  # empty: nothing to do
     assert L.arepi_combine_reduce(None, None, None, 4, 8, 64, None) == A.EINVAL
-    assert L.arepi_emu_peer_producer(None, None, None, None, 1, 256, 512, 2, 5, 128, 128, 0, None) == A.EINVAL
+    assert L.arepi_emu_peer_producer(None, None, None, None, 1, 256, 512, 2, 5, 128, 128, 0, 0, None) == A.EINVAL
 
 
 def test_binding_checks_dtype_before_pointers():
@@ -220,3 +223,17 @@ def test_owner_half_blocks_pair_on_the_model_shapes(M, N, R):
     assert len(owner_wgs) == (seg // (BM // 2)) * (-(-N // A.TILE_DIMS[tile][1]))
     for rb, cb, a0, alen, b0, blen in owner_wgs:
         assert a0 // seg == 0 and alen == BM // 2 and blen == BM // 2 and b0 // seg != 0
+
+
+@pytest.mark.parametrize("M,N,R", [(4096, 4096, 4), (1024, 7168, 8), (200, 520, 2)])
+def test_consume_option_plans_like_publication(M, N, R):
+    """AREPI_TILE_CONSUME_READY picks and lays out tiles as publication does
+    (both need every flag tile under one workgroup)."""
+    for ftm, ftn in ((128, 128), (32, 64)):
+        auto = A.gemm_rs_pick_tile(M, N, 2048, R, 0, ftm, ftn, publish=True)
+        if auto < 0:
+            assert A.gemm_rs_supports(M, N, 2048, R, 0, ftm, ftn, tile=A.TILE_CONSUME_READY) < 0
+            continue
+        ref = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=True)
+        got = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=False, tile=A.TILE_CONSUME_READY)
+        assert np.array_equal(ref, got)

@@ -82,7 +82,8 @@ def tiles_to_try(case, ftm, ftn):
 
 
 def tile_name(t):
-    return A.TILE_NAMES[t & ~A.TILE_PAIRED_ROWS] + ("/paired" if t & A.TILE_PAIRED_ROWS else "")
+    base = t & ~A.TILE_PAIRED_ROWS
+    return A.TILE_NAMES.get(base, "auto") + ("/paired" if t & A.TILE_PAIRED_ROWS else "")
 
 
 @pytest.mark.parametrize("owner", [0, 1])
@@ -184,7 +185,7 @@ def test_tp4_workload_prestaged_and_concurrent_producer():
     # partials in a shuffled tile order while the GEMM runs
     dev = device()
     tiles = oracle.flag_tiles(M, N, R, 128, 128)
-    for seed in (11, 12):
+    for seed, groups in ((11, 0), (12, 0), (13, 24)):
         order = torch.from_numpy(inputs.producer_order(R, owner, tiles, seed)).to(dev)
         src = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
         recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
@@ -197,7 +198,7 @@ def test_tp4_workload_prestaged_and_concurrent_producer():
         torch.cuda.synchronize()
         side = torch.cuda.Stream()
         main = torch.cuda.current_stream()
-        A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, stream=side)
+        A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, workgroups=groups, stream=side)
         A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, status=status, stream=main)
         torch.cuda.synchronize()
         assert int(status.item()) == 0, "a readiness wait timed out"
@@ -229,3 +230,47 @@ def test_timeout_reports_status_and_finishes():
     # send rows do not depend on the missing tile
     _, ref_send = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
     assert_bf16_close(res["send"][128:], ref_send[128:], "send after timeout")
+
+
+@pytest.mark.parametrize("M,N,K,R,owner,ftm,ftn,tile", [
+    (2048, 2048, 512, 4, 0, 128, 128, A.TILE_AUTO),
+    (1024, 7168, 256, 8, 3, 128, 128, A.TILE_256x256_W8 | A.TILE_PAIRED_ROWS),
+    (640, 1032, 200, 5, 3, 64, 128, A.TILE_AUTO),
+    (384, 264, 72, 3, 2, 32, 8, A.TILE_128x128_S4),
+])
+def test_consume_ready_leaves_ready_in_clear_for_the_next_call(M, N, K, R, owner, ftm, ftn, tile):
+    """With AREPI_TILE_CONSUME_READY the owner tiles clear the bits they waited
+    for: two calls in a row, each fed by the emulated producer on a second
+    stream, share one ready_in that nothing else clears; both match the oracle
+    and ready_in ends all zero."""
+    dev = device()
+    case = inputs.gemm_rs_case(M, N, K, R, owner=owner, seed=900 + M + R)
+    ref = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
+    seg = M // R
+    tiles = oracle.flag_tiles(M, N, R, ftm, ftn)
+    x, w = to_dev_bf16(case["x"]), to_dev_bf16(case["w"])
+    src = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
+    recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
+    rin = torch.zeros((R, A.gemm_rs_flag_words(M, N, R, ftm, ftn)), dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for call, seed in enumerate((31, 32)):
+        print("consume %s tile=%s call %d" % ((M, N, K, R, owner, ftm, ftn), tile_name(tile), call), flush=True)
+        for p in range(R):
+            if p != owner:
+                recv[p].zero_()
+        out = torch.full((seg, N), SENTINEL_FILL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        send = torch.full((M, N), SENTINEL_FILL, dtype=torch.int16, device=dev).view(torch.bfloat16)
+        rout = torch.zeros_like(rin)
+        order = torch.from_numpy(inputs.producer_order(R, owner, tiles, seed)).to(dev)
+        torch.cuda.synchronize()
+        A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, flag_tile_m=ftm, flag_tile_n=ftn,
+                            workgroups=16 * call, stream=side)
+        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, flag_tile_m=ftm,
+                        flag_tile_n=ftn, tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, "a readiness wait timed out"
+        assert not from_dev_u32(rin).any(), "ready_in bits left set"
+        res = dict(out=from_dev_bf16(out), send=from_dev_bf16(send), ready_out=from_dev_u32(rout))
+        check_against_oracle(case, res, ftm, ftn, what="consume call %d" % call, ref=ref)
