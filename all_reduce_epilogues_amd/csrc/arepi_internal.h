@@ -49,6 +49,10 @@ __device__ __forceinline__ void store16_nt(void *p, uint4 v) {
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
 }
 
+// gfx9 buffer-resource word 3 (raw, untyped 32-bit data format).
+constexpr int kBufferDword3 = 0x00020000;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 // Cache-policy operand of the direct-to-LDS load builtins for a streaming
 // (nt) load on gfx950 (checked against the emitted assembly).
 constexpr int kAuxNontemporal = 2;

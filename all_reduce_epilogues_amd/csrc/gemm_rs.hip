@@ -79,8 +79,6 @@ struct GemmRsParams {
     int consume;  // owner tiles clear the ready_in bits they waited for
 };
 
-// gfx9 buffer-resource word 3 (raw, untyped 32-bit data format).
-constexpr int kBufferDword3 = 0x00020000;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -107,7 +105,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource (base, no stride, num_records bytes, gfx9 word 3).
 __device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {

@@ -82,16 +82,34 @@ __global__ void __launch_bounds__(256) publish_kernel(const uint16_t *__restrict
     }
 }
 
-// Consumer.  First pass over a row: one plain 16-byte load per (pack, slot).
-// A kernel launch is an acquire at agent scope, so inside this launch a plain
-// load returns either the sentinel or data published during the launch -- never
-// an older payload.  Staging is touched once per launch, so these loads, the
-// re-arm stores and the output stores are nontemporal (streaming).  Packs that still show a sentinel are polled again with
-// device-coherent loads (which observe a producer running concurrently on
-// another XCD) until they land or the spin budget runs out.  Re-arm and output
-// are plain 16-byte stores; the kernel end releases them before any later
-// publication into the same staging.
-// NT threads per row: two waves up to 1024 packs (N <= 8192), four above.
+// Consumer.  A kernel launch is an acquire at agent scope, so inside this
+// launch a plain load of a staging pack returns either the sentinel or data
+// published during the launch -- never an older payload.
+//
+// Fast pass (no branches, so the compiler's memory-counter waits stay exact):
+// one nontemporal 16-byte buffer load per (pack, slot), the S loads of pack
+// j+1 in flight while pack j is checked and summed; a pack whose S slots all
+// arrived is re-armed at once.  Packs past the row end and slots past S use an
+// out-of-range offset: the load returns zeros (no sentinel, adds +0) and the
+// store is dropped.  A pack in which any slot still shows a sentinel is
+// neither summed for good nor re-armed; it is marked and redone after the fast
+// pass, slot by slot in the same order, polling with device-coherent loads
+// (which observe a producer running concurrently on another XCD) until the
+// pack lands or the spin budget runs out.  Every pack has exactly one consumer
+// thread, so re-arming needs no extra synchronisation; the kernel end
+// releases the re-arms before any later publication into the same staging.
+constexpr uint32_t kOob = 0x80000000u;  // at or past every resource's size (host-checked)
+
+__device__ __forceinline__ uint64_t lo64(const i32x4 v) { return (uint64_t)(uint32_t)v[0] | ((uint64_t)(uint32_t)v[1] << 32); }
+__device__ __forceinline__ uint64_t hi64(const i32x4 v) { return (uint64_t)(uint32_t)v[2] | ((uint64_t)(uint32_t)v[3] << 32); }
+__device__ __forceinline__ void add8(float (&acc)[8], uint64_t lo, uint64_t hi) {
+    const uint4 v = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+    float f[8];
+    unpack8(v, f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + f[e];
+}
+
 template <int PPT, int NT>
 __global__ void __launch_bounds__(NT) ar_rmsnorm_kernel(uint16_t *__restrict__ staging,
                                                         const uint16_t *__restrict__ gamma,
@@ -100,69 +118,86 @@ __global__ void __launch_bounds__(NT) ar_rmsnorm_kernel(uint16_t *__restrict__ s
                                                         uint32_t *status, int64_t spin_limit) {
     __shared__ float red[NT / 64];
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const int64_t packs = N / 8;
-    const int64_t plane = M * N;  // elements per slot
+    const int packs = (int)(N / 8);
+    // Byte offsets are 32-bit: 8 * M * N * 2 <= 2^31 (host-checked), so the
+    // offset of any of the 8 slots stays below kOob, and slots past S fall
+    // outside the resource (S planes) without a test.
+    const uint32_t plane2 = (uint32_t)(M * N * 2), row2 = (uint32_t)((int64_t)blockIdx.x * N * 2);
+    const __amdgpu_buffer_rsrc_t st_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)staging, 0, (int)(plane2 * (uint32_t)S), kBufferDword3);
     const bool sys = system != 0;
-    float s[PPT][8];
-    float ss = 0.f;
-    int64_t spins = 0;
-    bool gave_up = false;
-    const uint4 armed = make_uint4(kSent2, kSent2, kSent2, kSent2);
+    const i32x4 armed = {(int)kSent2, (int)kSent2, (int)kSent2, (int)kSent2};
+    // slot-0 offset of this thread's pack j, or kOob past the row end
+    auto pack_off = [&](int j) {
+        const int pk = tid + j * NT;
+        return pk < packs ? row2 + (uint32_t)pk * 16u : kOob;
+    };
 
-    // Two-deep pipeline over this thread's packs: the S slot loads of pack j+1
-    // are in flight while pack j is checked, summed and re-armed.
-    uint4 q[2][8];
-    auto issue = [&](int j, uint4 (&d)[8]) {
-        const int64_t pk = tid + (int64_t)j * NT;
-        const uint16_t *base = staging + row * N + (pk < packs ? pk : 0) * 8;
+    float s[PPT][8];
+    uint32_t bad = 0;  // bit j: pack j still showed a sentinel in the fast pass
+    i32x4 q[2][8];
+    auto issue = [&](int j, i32x4 (&d)[8]) {
+        const uint32_t o = pack_off(j);
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl)
-            if (sl < S && pk < packs) d[sl] = load16_nt(base + sl * plane);
+            d[sl] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(st_rs, o + (uint32_t)sl * plane2,
+                                                                                    0, kAuxNontemporal));
     };
     issue(0, q[0]);
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
         if (j + 1 < PPT) issue(j + 1, q[(j + 1) & 1]);
+        bool b = false;
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[j][e] = 0.f;
-        const int64_t pk = tid + (int64_t)j * NT;
-        if (pk < packs) {
-            uint16_t *base = staging + row * N + pk * 8;
 #pragma unroll
-            for (int sl = 0; sl < 8; ++sl) {
-                if (sl < S) {
-                    uint64_t lo = (uint64_t)q[j & 1][sl].x | ((uint64_t)q[j & 1][sl].y << 32);
-                    uint64_t hi = (uint64_t)q[j & 1][sl].z | ((uint64_t)q[j & 1][sl].w << 32);
-                    if (has_sentinel(lo) || has_sentinel(hi)) {
-                        // not (fully) landed yet: bounded coherent polling
-                        uint64_t *p64 = reinterpret_cast<uint64_t *>(base + sl * plane);
-                        while (!gave_up) {
-                            lo = load64_coherent(p64, sys);
-                            hi = load64_coherent(p64 + 1, sys);
-                            if (!has_sentinel(lo) && !has_sentinel(hi)) break;
-                            if (++spins > spin_limit) {
-                                gave_up = true;
-                                if (status) atomicOr(status, (uint32_t)AREPI_STATUS_TIMEOUT);
-                                break;
-                            }
-                            __builtin_amdgcn_s_sleep(2);
-                        }
+        for (int sl = 0; sl < 8; ++sl) {
+            const uint64_t lo = lo64(q[j & 1][sl]), hi = hi64(q[j & 1][sl]);
+            b |= has_sentinel(lo) | has_sentinel(hi);
+            add8(s[j], lo, hi);
+        }
+        bad |= (uint32_t)b << j;
+        const uint32_t o = b ? kOob : pack_off(j);
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl)
+            __builtin_amdgcn_raw_buffer_store_b128(armed, st_rs, o + (uint32_t)sl * plane2, 0, kAuxNontemporal);
+    }
+
+    // Slow pass: packs that had not fully landed, redone in slot order.
+    if (bad) {
+        int64_t spins = 0;
+        bool gave_up = false;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            if (!((bad >> j) & 1u)) continue;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[j][e] = 0.f;
+            uint16_t *base = staging + (int64_t)blockIdx.x * N + (int64_t)(tid + j * NT) * 8;
+            for (int sl = 0; sl < S; ++sl) {
+                uint64_t *p64 = reinterpret_cast<uint64_t *>(base + (int64_t)sl * M * N);
+                uint64_t lo = load64_coherent(p64, sys), hi = load64_coherent(p64 + 1, sys);
+                while (!gave_up && (has_sentinel(lo) || has_sentinel(hi))) {
+                    if (++spins > spin_limit) {
+                        gave_up = true;
+                        if (status) atomicOr(status, (uint32_t)AREPI_STATUS_TIMEOUT);
+                        break;
                     }
-                    const uint4 v = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
-                    float f[8];
-                    unpack8(v, f);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s[j][e] = s[j][e] + f[e];
-                    // re-arm the consumed pack
-                    store16_nt(base + sl * plane, armed);
+                    __builtin_amdgcn_s_sleep(2);
+                    lo = load64_coherent(p64, sys);
+                    hi = load64_coherent(p64 + 1, sys);
                 }
+                add8(s[j], lo, hi);
+                store16_nt(base + (int64_t)sl * M * N, make_uint4(kSent2, kSent2, kSent2, kSent2));
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = ss + s[j][e] * s[j][e];
         }
     }
-    // workgroup sum of s^2
+
+    // workgroup sum of s^2 (pack-major, then element order, per thread)
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = ss + s[j][e] * s[j][e];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
     if ((tid & 63) == 0) red[tid >> 6] = ss;
@@ -171,17 +206,27 @@ __global__ void __launch_bounds__(NT) ar_rmsnorm_kernel(uint16_t *__restrict__ s
 #pragma unroll
     for (int w = 1; w < NT / 64; ++w) tot = tot + red[w];
     const float r = 1.0f / sqrtf(tot / (float)N + eps);
+
+    const __amdgpu_buffer_rsrc_t g_rs = __builtin_amdgcn_make_buffer_rsrc((void *)gamma, 0, (int)(N * 2), kBufferDword3);
+    const __amdgpu_buffer_rsrc_t o_rs = __builtin_amdgcn_make_buffer_rsrc((void *)out, 0, (int)plane2, kBufferDword3);
+    i32x4 g[PPT];
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
-        const int64_t pk = tid + (int64_t)j * NT;
-        if (pk < packs) {
-            const uint4 g = *reinterpret_cast<const uint4 *>(gamma + pk * 8);
-            float gf[8], y[8];
-            unpack8(g, gf);
+        const int pk = tid + j * NT;
+        g[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             g_rs, pk < packs ? (uint32_t)pk * 16u : kOob, 0, 0));
+    }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = (s[j][e] * r) * gf[e];
-            store16_nt(out + row * N + pk * 8, pack8(y));
-        }
+    for (int j = 0; j < PPT; ++j) {
+        const int pk = tid + j * NT;
+        float gf[8], y[8];
+        unpack8(make_uint4((uint32_t)g[j][0], (uint32_t)g[j][1], (uint32_t)g[j][2], (uint32_t)g[j][3]), gf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (s[j][e] * r) * gf[e];
+        const uint4 o = pack8(y);
+        const i32x4 ov = {(int)o.x, (int)o.y, (int)o.z, (int)o.w};
+        __builtin_amdgcn_raw_buffer_store_b128(ov, o_rs, pk < packs ? row2 + (uint32_t)pk * 16u : kOob, 0,
+                                               kAuxNontemporal);
     }
 }
 
@@ -241,7 +286,8 @@ extern "C" int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma
     if (!staging || !gamma || !out) return bad("staging, gamma and out must be non-NULL");
     if (!aligned16(staging) || !aligned16(gamma) || !aligned16(out))
         return bad("staging, gamma and out must be 16-byte aligned");
-    if (M > (int64_t)1 << 31) return fail(AREPI_EUNSUPPORTED, "arepi_ar_rmsnorm_lamport: M above 2^31");
+    if (M * N * 2 * 8 > (int64_t)1 << 31)
+        return fail(AREPI_EUNSUPPORTED, "arepi_ar_rmsnorm_lamport: one staging slot (M*N*2 bytes) must be at most 256 MiB");
     const int64_t packs = N / 8;
     const int64_t lim = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
     const int sys = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
