@@ -51,6 +51,8 @@ def _load():
     vp = ctypes.c_void_p
     lib.oracle_gemm_rs.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i64, i64]
     lib.oracle_gemm_rs.restype = i32
+    lib.oracle_gemm_rs_ring.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i64, i64]
+    lib.oracle_gemm_rs_ring.restype = i32
     lib.oracle_flag_tiles.argtypes = [i64, i64, i32, i64, i64]
     lib.oracle_flag_tiles.restype = i64
     lib.oracle_flag_words.argtypes = [i64, i64, i32, i64, i64]
@@ -138,6 +140,46 @@ def gemm_rs(x, w, recv, R: int, owner: int, rows=None, want_send: bool = True):
                                 _p(send) if send is not None else None, M, N, K, R, owner, r0, r1)
     if rc != 0:
         raise ValueError("oracle_gemm_rs rejected its arguments")
+    return out, send
+
+
+def gemm_rs_ring(x, w, upstream, R: int, owner: int, rows=None, want_send: bool = True):
+    """Push-ring form of one rank's GEMM + reduce-scatter epilogue.
+
+    upstream: list of R arrays uint16 [M/R,N]; upstream[d] is the running
+    partial of segment d from the upstream rank (the entry of the segment this
+    rank starts, (owner - 1) mod R, may be None).  Returns (out, send) like
+    gemm_rs().
+    """
+    x, w = _u16(x), _u16(w)
+    M, K = x.shape
+    K2, N = w.shape
+    if K2 != K:
+        raise ValueError("x is [M,K] and w is [K,N]")
+    if M % R:
+        raise ValueError("M must be a multiple of R")
+    seg = M // R
+    chain = (owner + R - 1) % R
+    keep = []
+    ptrs = (ctypes.c_void_p * R)()
+    for d in range(R):
+        if R == 1 or d == chain or upstream[d] is None:
+            if R > 1 and d != chain:
+                raise ValueError("upstream[%d] is needed" % d)
+            ptrs[d] = None
+            continue
+        ud = _u16(upstream[d])
+        if ud.shape != (seg, N):
+            raise ValueError("upstream[%d] must be [%d,%d]" % (d, seg, N))
+        keep.append(ud)
+        ptrs[d] = ud.ctypes.data
+    out = np.zeros((seg, N), dtype=np.uint16)
+    send = np.zeros((M, N), dtype=np.uint16) if want_send else None
+    r0, r1 = (0, M) if rows is None else rows
+    rc = _load().oracle_gemm_rs_ring(_p(x), _p(w), ctypes.cast(ptrs, ctypes.c_void_p), _p(out),
+                                     _p(send) if send is not None else None, M, N, K, R, owner, r0, r1)
+    if rc != 0:
+        raise ValueError("oracle_gemm_rs_ring rejected its arguments")
     return out, send
 
 

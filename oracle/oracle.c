@@ -154,6 +154,71 @@ int oracle_gemm_rs(const uint16_t *x, const uint16_t *w, const uint16_t *const *
     return bad ? -1 : 0;
 }
 
+/* ---- push-ring form of the same reduce-scatter ([P1] description) ----------
+ *
+ * In the ring of [P1] each rank takes the running partial of a segment from
+ * its upstream neighbour, adds its own partial and pushes the sum downstream;
+ * the owner of the segment is the last rank of that chain and ends with the
+ * full sum.  Reading taken here: rank r receives from rank r-1 and sends to
+ * rank r+1 (mod R), so the chain of segment d runs d+1, d+2, ..., d; rank r
+ * starts the chain of segment chain = (r - 1) mod R, which has no upstream
+ * partial; the partials travel as bf16 (rounded at every hop).
+ *
+ * upstream is an array of R pointers to [seg,N] bf16 buffers: upstream[d] is
+ * the running partial of segment d received from the upstream rank
+ * (upstream[chain] is never read; with R = 1 nothing is read).
+ *     out[i,n]  = bf16( C_r[owner*seg + i, n] + upstream[owner][i,n] )
+ *     send[i,n] = bf16( C_r[i,n] + upstream[d][i - d*seg, n] )  (row i in segment d)
+ *     send[i,n] = bf16( C_r[i,n] )                                (row i in segment chain)
+ * C_r is accumulated exactly as in oracle_gemm_rs (fp32, k ascending), and
+ * the local accumulator comes first in every add.
+ */
+int oracle_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const uint16_t *const *upstream,
+                        uint16_t *out, uint16_t *send, int64_t M, int64_t N, int64_t K, int R,
+                        int owner, int64_t row_begin, int64_t row_end) {
+    if (M < 0 || N < 0 || K < 0 || R < 1 || owner < 0 || owner >= R) return -1;
+    if (M % R != 0) return -1;
+    if (row_begin < 0 || row_end > M || row_begin > row_end) return -1;
+    const int64_t seg = M / R;
+    const int chain = (owner + R - 1) % R;
+    int bad = 0;
+#pragma omp parallel
+    {
+        float *acc = (float *)malloc((size_t)(N > 0 ? N : 1) * sizeof(float));
+        if (!acc) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t i = row_begin; i < row_end; ++i) {
+                for (int64_t n = 0; n < N; ++n) acc[n] = 0.0f;
+                for (int64_t k = 0; k < K; ++k) {
+                    const float xv = bf16_to_f32(x[i * K + k]);
+                    const uint16_t *wrow = w + k * N;
+                    for (int64_t n = 0; n < N; ++n) acc[n] = acc[n] + xv * bf16_to_f32(wrow[n]);
+                }
+                const int64_t d = i / seg, li = i - d * seg;
+                const int adds = R > 1 && d != chain;
+                if (d == owner) {
+                    for (int64_t n = 0; n < N; ++n) {
+                        float t = acc[n];
+                        if (adds) t = t + bf16_to_f32(upstream[d][li * N + n]);
+                        out[li * N + n] = f32_to_bf16_rne(t);
+                    }
+                } else if (send) {
+                    for (int64_t n = 0; n < N; ++n) {
+                        float t = acc[n];
+                        if (adds) t = t + bf16_to_f32(upstream[d][li * N + n]);
+                        send[i * N + n] = f32_to_bf16_rne(t);
+                    }
+                }
+            }
+            free(acc);
+        }
+    }
+    return bad ? -1 : 0;
+}
+
 /* ---- per-tile readiness bitmask ([P1] title and description) ---------------
  *
  * Each segment is cut into flag tiles of ftm x ftn (clipped at the segment's
