@@ -67,6 +67,9 @@ def lib():
             "arepi_gemm_rs_schedule": ([i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, i64], i64),
             "arepi_gemm_rs_fused": ([vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
                                      u32p, i64, vp], i32),
+            "arepi_gemm_rs_ring_supports": ([i64, i64, i64, i32, i32, i32, i32, i32, i32], i32),
+            "arepi_gemm_rs_ring": ([vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                    u32p, i64, vp], i32),
             "arepi_lamport_prefill": ([vp, i64, vp], i32),
             "arepi_lamport_publish": ([vp, vp, vp, i32, i64, i64, i32, i32, i32, vp], i32),
             "arepi_ar_rmsnorm_lamport": ([vp, vp, vp, i64, i64, i32, f32, i32, u32p, i64, vp], i32),
@@ -201,6 +204,53 @@ def gemm_rs_fused(x, w, recv, ready_in, out, R: int, owner: int, send=None, read
                                    flag_tile_m, flag_tile_n, scope, tile, _ptr(status), spin_limit,
                                    _stream(stream))
     _check(rc, "gemm_rs_fused")
+
+
+def gemm_rs_ring_supports(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publish=False,
+                          tile=TILE_AUTO) -> int:
+    """0 when the push-ring form supports the shape, else the negative status."""
+    return lib().arepi_gemm_rs_ring_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish), tile)
+
+
+def gemm_rs_ring(x, w, upstream, ready_in, out, send, R: int, owner: int, ready_out=None,
+                 flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT,
+                 tile: int = TILE_AUTO, status=None, spin_limit: int = 0, stream=None):
+    """One hop of the push ring: out = bf16(X.W owner rows + upstream[owner]),
+    send rows of segment d = bf16(X.W + upstream[d]) (the chain segment
+    (owner-1) mod R without upstream); see include/arepi.h."""
+    _bf16(x, "x")
+    M, K = x.shape
+    _bf16(w, "w")
+    if w.shape[0] != K:
+        raise ValueError("w must be [K=%d, N], got %s" % (K, tuple(w.shape)))
+    N = w.shape[1]
+    if M % R:
+        raise ValueError("M=%d is not a multiple of R=%d" % (M, R))
+    seg = M // R
+    chain = (owner + R - 1) % R
+    _bf16(out, "out", (seg, N))
+    _bf16(send, "send", (M, N))
+    words = gemm_rs_flag_words(M, N, R, flag_tile_m, flag_tile_n)
+    if ready_in is not None:
+        _flags(ready_in, "ready_in", (R, words))
+    if ready_out is not None:
+        _flags(ready_out, "ready_out", (R, words))
+    if status is not None:
+        _flags(status, "status", (1,))
+    if len(upstream) != R:
+        raise ValueError("upstream must list R=%d buffers (entry (owner-1) mod R may be None)" % R)
+    ptrs = (ctypes.c_void_p * R)()
+    for d in range(R):
+        if (R > 1 and d == chain) or upstream[d] is None:
+            ptrs[d] = None
+            continue
+        _bf16(upstream[d], "upstream[%d]" % d, (seg, N))
+        ptrs[d] = upstream[d].data_ptr()
+    rc = lib().arepi_gemm_rs_ring(_ptr(x), _ptr(w), ctypes.cast(ptrs, ctypes.c_void_p), _ptr(ready_in),
+                                  _ptr(out), _ptr(send), _ptr(ready_out), M, N, K, R, owner,
+                                  flag_tile_m, flag_tile_n, scope, tile, _ptr(status), spin_limit,
+                                  _stream(stream))
+    _check(rc, "gemm_rs_ring")
 
 
 def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N: int,

@@ -71,6 +71,17 @@ def gemm_rs_case(M: int, N: int, K: int, R: int, owner: int = 0, seed: int = 100
     return dict(x=x, w=w, recv=recv, M=M, N=N, K=K, R=R, owner=owner, seed=seed)
 
 
+def gemm_rs_ring_case(M: int, N: int, K: int, R: int, owner: int = 0, seed: int = 1002, **kw) -> dict:
+    """X_r, W_r and the running partials received from upstream in the push
+    ring: up[d] [M/R,N] for every segment d except the one this rank starts,
+    (owner - 1) mod R, whose entry is None.  Same draws as gemm_rs_case with
+    that segment in the owner's place."""
+    c = gemm_rs_case(M, N, K, R, owner=(owner + R - 1) % R, seed=seed, **kw)
+    c["up"] = c.pop("recv")
+    c["owner"] = owner
+    return c
+
+
 WORKLOADS = {
     1: dict(M=256, N=512, K=256, R=2, dist="uniform"),
     2: dict(M=4096, N=4096, K=2048, R=4, dist="normal"),

@@ -8,8 +8,10 @@ producer on a second stream in shuffled order -- as TFLOP/s of the whole step
 
 Also reported in the same run: the Lamport AR+RMSNorm consumer (8 x
 [4096,7168]) and the weighted top-8 combine ([4096,8,7168]) as GB/s of
-algorithmic bytes, each against the 8 TB/s HBM peak; with --sweep the tp=8
-sweep (M = 256..8192, N=7168, K=2048) and the pre-staged tp=4 kernel.
+algorithmic bytes, each against the 8 TB/s HBM peak; the pre-staged tp=4
+kernel; the push-ring form of the same GEMM (one hop: the producer landing the
+upstream partials beside it, and pre-staged); with --sweep the tp=8 sweep
+(M = 256..8192, N=7168, K=2048) in both forms.
 
 `cpu_baseline` times the CPU oracle (oracle/, test infrastructure) on a
 bounded row sample of the headline workload.
@@ -83,15 +85,17 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sweep", action="store_true", help="also time the tp=8 sweep and the pre-staged tp=4 kernel")
-    ap.add_argument("--only", default=None, choices=[None, "gemm_rs", "gemm_rs_prestaged", "lamport", "combine"],
+    ap.add_argument("--only", default=None, choices=[None, "gemm_rs", "gemm_rs_prestaged", "gemm_rs_ring",
+                                                   "gemm_rs_ring_prestaged", "lamport", "combine"],
                     help="run a single path (used for per-kernel profiles; counter collection serializes "
                          "kernels, so the GEMM's counters are taken pre-staged, without the producer stream)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     return ap.parse_args()
 
 
-def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
-    """tp=4 share; a producer stream lands the peers while the GEMM runs.
+def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False):
+    """tp=4 share; a producer stream lands the peers while the GEMM runs
+    (ring=True: the push-ring hop, the producer landing the upstream partials).
 
     The main stream runs only the GEMMs, back to back.  Each consumes its
     ready_in bits (the owner tiles clear what they waited for), so ready_in is
@@ -105,19 +109,26 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
     HIP events recorded on its stream just before and after each launch.
     """
     dev = torch.device("cuda:0")
-    case = inputs.workload_gemm_rs(2)
+    if ring:  # push-ring hop: upstream partials of every segment but the chain one
+        case = inputs.gemm_rs_ring_case(**dict(inputs.WORKLOADS[2], M=4096), seed=1002)
+    else:
+        case = inputs.workload_gemm_rs(2)
     M, N, K, R, owner = case["M"], case["N"], case["K"], case["R"], case["owner"]
     seg = M // R
+    # segment whose partial does not arrive: the owner's own (direct sum) or
+    # the one this rank starts (ring)
+    absent = (owner + R - 1) % R if ring else owner
+    parts = case["up"] if ring else case["recv"]
 
     def up(a):
         return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
 
     x, w = up(case["x"]), up(case["w"])
-    src = [None if p == owner else up(case["recv"][p]) for p in range(R)]
-    recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
+    src = [None if p == absent else up(parts[p]) for p in range(R)]
+    recv = [None if p == absent else torch.zeros_like(src[p]) for p in range(R)]
     words = A.gemm_rs_flag_words(M, N, R)
     tiles = ((seg + 127) // 128) * ((N + 127) // 128)
-    orders = [torch.from_numpy(inputs.producer_order(R, owner, tiles, 2000 + i)).to(dev) for i in range(4)]
+    orders = [torch.from_numpy(inputs.producer_order(R, absent, tiles, 2000 + i)).to(dev) for i in range(4)]
     rin = torch.zeros((R, words), dtype=torch.int32, device=dev)
     rout = torch.zeros((R, words), dtype=torch.int32, device=dev)
     out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
@@ -134,10 +145,14 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
     def step(i):
         if i > 0:
             H.wait(side, ev_ge[i - 1])
-        A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, owner, M, N, stream=side)
+        A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, absent, M, N, stream=side)
         H.record(ev_gs[i], main)
-        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout,
-                        tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
+        if ring:
+            A.gemm_rs_ring(x, w, recv, rin, out, send, R, owner, ready_out=rout,
+                           tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
+        else:
+            A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout,
+                            tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
         H.record(ev_ge[i], main)
 
     for i in range(warmup):
@@ -158,23 +173,33 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup):
                 M=M, N=N, K=K, R=R)
 
 
-def gemm_rs_prestaged(A, inputs, torch, steps, warmup, num, M=None):
+def gemm_rs_prestaged(A, inputs, torch, steps, warmup, num, M=None, ring=False):
+    """GEMM + reduce-scatter epilogue with every partial landed beforehand (all
+    ready bits set): the kernel alone.  ring=True times the push-ring hop."""
     dev = torch.device("cuda:0")
-    case = inputs.workload_gemm_rs(num, M=M)
+    if ring:
+        spec = dict(inputs.WORKLOADS[num])
+        if M is not None:
+            spec["M"] = M
+        case = inputs.gemm_rs_ring_case(seed=1000 + num, **spec)
+    else:
+        case = inputs.workload_gemm_rs(num, M=M)
     M, N, K, R, owner = case["M"], case["N"], case["K"], case["R"], case["owner"]
     seg = M // R
+    absent = (owner + R - 1) % R if ring else owner
+    parts = case["up"] if ring else case["recv"]
 
     def up(a):
         return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
 
     x, w = up(case["x"]), up(case["w"])
-    recv = [None if p == owner else up(case["recv"][p]) for p in range(R)]
+    recv = [None if p == absent else up(parts[p]) for p in range(R)]
     words = A.gemm_rs_flag_words(M, N, R)
     tiles = ((seg + 127) // 128) * ((N + 127) // 128)
     import numpy as np
     full = np.zeros((R, words), np.uint32)
     for p in range(R):
-        if p != owner:
+        if p != absent:
             for t in range(tiles):
                 full[p, t // 32] |= np.uint32(1 << (t % 32))
     rin = torch.from_numpy(full.view(np.int32)).to(dev)
@@ -183,12 +208,19 @@ def gemm_rs_prestaged(A, inputs, torch, steps, warmup, num, M=None):
     send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     tile = A.gemm_rs_pick_tile(M, N, K, R, owner, publish=True)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def call():
+        if ring:
+            A.gemm_rs_ring(x, w, recv, rin, out, send, R, owner, ready_out=rout, tile=tile)
+        else:
+            A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile)
+
     for _ in range(warmup):
-        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile)
+        call()
     torch.cuda.synchronize()
     s.record()
     for _ in range(steps):
-        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile)
+        call()
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / steps
@@ -322,9 +354,19 @@ def main():
         secondary["combine_reduce"] = combine(A, inputs, torch, max(10, a.steps // 2), 3)
     if a.only in (None, "gemm_rs", "gemm_rs_prestaged"):
         secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2)
+    if a.only in (None, "gemm_rs_ring"):
+        r = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, ring=True)
+        secondary["gemm_rs_ring_tp4_step"] = dict(ms_per_step=r["ms_per_step"], tflops=r["tflops"],
+                                                  kernel_ms=r["gemm_ms"], kernel_tflops=r["gemm_tflops"],
+                                                  frac_mfma=r["gemm_tflops"] / PEAK_BF16_TFLOPS, tile=r["tile"])
+    if a.only in (None, "gemm_rs_ring", "gemm_rs_ring_prestaged"):
+        secondary["gemm_rs_ring_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2,
+                                                                    ring=True)
     if a.sweep:
         secondary["gemm_rs_tp8_sweep"] = [gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 3, M=m)
                                          for m in inputs.TP8_M_SWEEP]
+        secondary["gemm_rs_ring_tp8_sweep"] = [gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 3, M=m,
+                                                                 ring=True) for m in inputs.TP8_M_SWEEP]
     line = {
         "metric": "GEMM-RS TFLOP/s + % bf16 MFMA peak; combine/RMSNorm GB/s + % HBM peak",
         "value": head["tflops"] if head else None,

@@ -7,6 +7,8 @@
  *   arepi_gemm_rs_fused      row-parallel bf16 GEMM whose epilogue finishes the
  *                            reduce-scatter of this rank's owner segment, gated
  *                            per flag tile by a readiness bitmask.
+ *   arepi_gemm_rs_ring       the same GEMM as one hop of a push-ring
+ *                            reduce-scatter (one upstream partial per row).
  *   arepi_ar_rmsnorm_lamport all-reduce combine + RMSNorm where the data is its
  *                            own arrival flag (Lamport -0.0 sentinel).
  *   arepi_combine_reduce     weighted top-k combine of expert outputs.
@@ -148,6 +150,44 @@ int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const uint16_t *co
                         uint32_t *ready_out, int64_t M, int64_t N, int64_t K, int R, int owner,
                         int flag_tile_m, int flag_tile_n, int scope, int tile_cfg,
                         uint32_t *status, int64_t spin_limit, arepi_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * GEMM + reduce-scatter epilogue, push-ring form.
+ *
+ * Defined by DeepGEMM PR #1 "Fused ring RS: per-tile bitmask + drain-ring with
+ * owner-boundary flush" (description): the reduce-scatter runs as a ring in
+ * which each rank adds its own partial tile to the running partial it
+ * received from upstream and pushes the sum downstream; the owner of a segment
+ * is the last rank of its chain.  Reading taken: rank r receives from r-1 and
+ * sends to r+1 (mod R), so the segment this rank starts is
+ * chain = (owner - 1) mod R, and partials travel as bf16.
+ *
+ * Arguments as for arepi_gemm_rs_fused, except:
+ *   upstream HOST array of R device pointers; upstream[d] is bf16 [M/R,N], the
+ *            running partial of segment d from the upstream rank;
+ *            upstream[chain] is ignored (with R = 1 nothing is read).
+ *   ready_in u32 [R][words]; bit t of entry d says flag tile t of upstream[d]
+ *            has landed (consumed as in arepi_gemm_rs_fused with
+ *            AREPI_TILE_CONSUME_READY).
+ *   out      bf16 [M/R,N]: out[i,n] = bf16(C[owner*M/R + i, n] + upstream[owner][i,n]).
+ *   send     bf16 [M,N], required: a row i of segment d != owner receives
+ *            bf16(C[i,n] + upstream[d][i - d*M/R, n]), or bf16(C[i,n]) when
+ *            d == chain (one fp32 add, then round-to-nearest-even).
+ *   ready_out as for arepi_gemm_rs_fused (every segment d != owner).
+ * Every tile that adds an upstream partial waits for its ready_in bits with an
+ * acquire at `scope`.  Tiles run segment by segment in ring order: chain first,
+ * then chain-1, ..., owner last.
+ * Constraints: those of arepi_gemm_rs_fused, plus (M/R) % 8 == 0 when R > 1;
+ * AREPI_TILE_PAIRED_ROWS is refused (EUNSUPPORTED).
+ * ------------------------------------------------------------------------ */
+int arepi_gemm_rs_ring_supports(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
+                                int flag_tile_n, int publish, int tile_cfg);
+
+int arepi_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const uint16_t *const *upstream,
+                       uint32_t *ready_in, uint16_t *out, uint16_t *send, uint32_t *ready_out,
+                       int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
+                       int flag_tile_n, int scope, int tile_cfg, uint32_t *status,
+                       int64_t spin_limit, arepi_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * Lamport all-reduce + RMSNorm.

@@ -237,3 +237,42 @@ def test_consume_option_plans_like_publication(M, N, R):
         ref = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=True)
         got = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=False, tile=A.TILE_CONSUME_READY)
         assert np.array_equal(ref, got)
+
+
+@pytest.mark.parametrize("M,N,R,owner", [(256, 512, 2, 0), (4096, 4096, 4, 0), (256, 7168, 8, 0), (96, 72, 4, 2)])
+def test_ring_supports_follows_the_direct_form(M, N, R, owner):
+    """The push-ring form accepts what the direct form accepts (contiguous
+    rows), refuses paired half-blocks, and needs 8-row-aligned segments."""
+    for tile in TILE_DIMS:
+        for publish in (False, True):
+            d = A.gemm_rs_supports(M, N, 64, R, owner, 128, 128, publish=publish, tile=tile)
+            r = A.gemm_rs_ring_supports(M, N, 64, R, owner, 128, 128, publish=publish, tile=tile)
+            assert r == d, (tile, publish, A.last_error())
+        assert A.gemm_rs_ring_supports(M, N, 64, R, owner, 128, 128, tile=tile | A.TILE_PAIRED_ROWS) == \
+            A.EUNSUPPORTED
+        assert "direct form only" in A.last_error()
+
+
+def test_ring_rejects_unaligned_segments_and_bad_pointers():
+    assert A.gemm_rs_ring_supports(24, 8, 16, 8, 7, 3, 8) == A.EUNSUPPORTED
+    assert "multiple of 8" in A.last_error()
+    assert A.gemm_rs_ring_supports(24, 8, 16, 1, 0, 3, 8) == 0  # one rank: no segments to align
+    L = A.lib()
+    vp = ctypes.c_void_p
+    buf = ctypes.create_string_buffer(64)
+    p = vp(ctypes.addressof(buf) + (-ctypes.addressof(buf)) % 16)
+    # R=4, owner=1: chain segment 0 may be NULL, segment 3 may not
+    up = (vp * 4)(None, p, p, None)
+    rc = L.arepi_gemm_rs_ring(p, p, ctypes.cast(up, vp), p, p, p, None, 256, 512, 256, 4, 1, 128, 128,
+                              0, 0, None, 0, None)
+    assert rc == A.EINVAL and "upstream[3]" in A.last_error()
+    up = (vp * 4)(None, p, p, p)
+    rc = L.arepi_gemm_rs_ring(p, p, ctypes.cast(up, vp), p, p, None, None, 256, 512, 256, 4, 1, 128, 128,
+                              0, 0, None, 0, None)
+    assert rc == A.EINVAL and "send" in A.last_error()
+    rc = L.arepi_gemm_rs_ring(p, p, ctypes.cast(up, vp), None, p, p, None, 256, 512, 256, 4, 1, 128, 128,
+                              0, 0, None, 0, None)
+    assert rc == A.EINVAL and "ready_in" in A.last_error()
+    rc = L.arepi_gemm_rs_ring(p, p, ctypes.cast(up, vp), p, p, p, None, 256, 512, 256, 4, 1, 128, 128,
+                              3, 0, None, 0, None)
+    assert rc == A.EINVAL and "scope=3" in A.last_error()

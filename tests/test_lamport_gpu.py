@@ -37,10 +37,15 @@ def publish_and_consume(case, sequential=True, status=None):
         published = from_dev_bf16(st)
         A.ar_rmsnorm_lamport(st, gamma, out, case["eps"], status=status)
     else:
+        # Streams are spread over a few hardware queues, and two streams can
+        # share one, which runs its work in submission order: the publisher is
+        # submitted first so that a shared queue serialises the pair instead of
+        # leaving the consumer to wait for work queued behind it.  On separate
+        # queues the consumer starts while the publisher is still landing tiles.
         side = torch.cuda.Stream()
         published = None
-        A.ar_rmsnorm_lamport(st, gamma, out, case["eps"], status=status)      # consumer first: it spins
         A.lamport_publish(src, st, order, case["tile_m"], case["tile_n"], stream=side)
+        A.ar_rmsnorm_lamport(st, gamma, out, case["eps"], status=status)
     torch.cuda.synchronize()
     return dict(out=from_dev_bf16(out), staging=from_dev_bf16(st), published=published)
 
@@ -79,7 +84,7 @@ def test_sentinel_words_in_the_data_are_canonicalised():
 
 
 def test_concurrent_publication_gives_identical_bits():
-    case = inputs.lamport_case(8, 256, 7168, seed=91)
+    case = inputs.lamport_case(8, 1024, 7168, seed=91)  # publication outlasts the consumer's start
     seq = publish_and_consume(case)
     status = torch.zeros(1, dtype=torch.int32, device=device())
     conc = publish_and_consume(case, sequential=False, status=status)
