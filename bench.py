@@ -93,7 +93,7 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False):
+def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs=0):
     """tp=4 share; a producer stream lands the peers while the GEMM runs
     (ring=True: the push-ring hop, the producer landing the upstream partials).
 
@@ -145,7 +145,8 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False):
     def step(i):
         if i > 0:
             H.wait(side, ev_ge[i - 1])
-        A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, absent, M, N, stream=side)
+        A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, absent, M, N, workgroups=producer_wgs,
+                            stream=side)
         H.record(ev_gs[i], main)
         if ring:
             A.gemm_rs_ring(x, w, recv, rin, out, send, R, owner, ready_out=rout,
@@ -310,21 +311,29 @@ def cpu_baseline(inputs, budget_s=10.0):
 
 
 COUNTERS_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "gemm_rs_tp4_counters.txt")
-KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "all_reduce_epilogues_amd", "csrc",
-                             "gemm_rs.hip")
+# the kernel body and the direct-form entry (the counters go stale when either changes)
+KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "all_reduce_epilogues_amd", "csrc", f)
+                  for f in ("gemm_rs_impl.h", "gemm_rs.hip")]
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(tile):
     """HBM-side bytes per launch of the GEMM kernel from the stored rocprofv3
     FETCH_SIZE / WRITE_SIZE passes (scaled by the copy-kernel calibration), or
     None when the kernel source or the tile has changed since they were taken."""
-    import hashlib
     try:
         with open(COUNTERS_FILE) as f:
             rec = dict(line.split(": ", 1) for line in f.read().splitlines()
                        if line and not line.startswith("#") and ": " in line)
-        with open(KERNEL_SOURCE, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
+        digest = kernel_source_digest()
     except OSError:
         return None
     if rec.get("source_sha256", "").strip() != digest or rec.get("tile", "").strip() != tile:
