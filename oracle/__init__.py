@@ -66,6 +66,10 @@ def _load():
     lib.oracle_ar_rmsnorm.argtypes = [vp, vp, vp, i64, i64, i32, f32, i64, i64]
     lib.oracle_ar_rmsnorm.restype = i32
     lib.oracle_combine.argtypes = [vp, vp, vp, i64, i32, i64, i64, i64]
+    lib.oracle_lamport_reduce.argtypes = [vp, vp, i64, i64, i32, i64, i64]
+    lib.oracle_lamport_reduce.restype = i32
+    lib.oracle_ar_rmsnorm_2phase.argtypes = [vp, vp, vp, i64, i64, i32, f32, i64, i64]
+    lib.oracle_ar_rmsnorm_2phase.restype = i32
     lib.oracle_combine.restype = i32
     lib.oracle_bf16_from_f32.argtypes = [vp, vp, i64]
     lib.oracle_bf16_from_f32.restype = None
@@ -222,6 +226,33 @@ def ar_rmsnorm(src, gamma, eps: float = 1e-6, rows=None) -> np.ndarray:
     r0, r1 = (0, M) if rows is None else rows
     if _load().oracle_ar_rmsnorm(_p(src), _p(gamma), _p(out), M, N, S, eps, r0, r1) != 0:
         raise ValueError("oracle_ar_rmsnorm rejected its arguments")
+    return out
+
+
+def lamport_reduce(x, rows=None) -> np.ndarray:
+    """Phase A of the two-phase Lamport path: T = canon(bf16(sum over ranks)).
+    x: uint16 [R,M,N] (the ranks' inputs).  Returns uint16 [M,N] (rows outside
+    `rows` left zero)."""
+    x = _u16(x)
+    R, M, N = x.shape
+    t = np.zeros((M, N), dtype=np.uint16)
+    r0, r1 = (0, M) if rows is None else rows
+    if _load().oracle_lamport_reduce(_p(x), _p(t), M, N, R, r0, r1) != 0:
+        raise ValueError("oracle_lamport_reduce rejected its arguments")
+    return t
+
+
+def ar_rmsnorm_2phase(x, gamma, eps: float = 1e-6, rows=None) -> np.ndarray:
+    """Two-phase Lamport AR + RMSNorm: RMSNorm of the bf16-rounded sum.
+    x: uint16 [R,M,N]; gamma uint16 [N]."""
+    x, gamma = _u16(x), _u16(gamma)
+    R, M, N = x.shape
+    if gamma.shape != (N,):
+        raise ValueError("gamma must be [N]")
+    out = np.zeros((M, N), dtype=np.uint16)
+    r0, r1 = (0, M) if rows is None else rows
+    if _load().oracle_ar_rmsnorm_2phase(_p(x), _p(gamma), _p(out), M, N, R, eps, r0, r1) != 0:
+        raise ValueError("oracle_ar_rmsnorm_2phase rejected its arguments")
     return out
 
 

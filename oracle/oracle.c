@@ -310,6 +310,57 @@ int oracle_ar_rmsnorm(const uint16_t *src, const uint16_t *gamma, uint16_t *out,
     return bad ? -1 : 0;
 }
 
+/* ---- two-phase Lamport AR + RMSNorm ([P4] Approach: phase A, then phase B) ---
+ *
+ * Phase A is a reduce-scatter with cross-device stores: the [M,N] tensor is
+ * cut into R parts, the rank owning a part adds the R ranks' partials of its
+ * elements, rounds the sum once to bf16, maps -0.0 to +0.0 and stores the
+ * result into every rank's staging.  Which rank owns which part changes no
+ * value (each element's sum is the same), so once every part has landed each
+ * staging holds
+ *     T[i,n] = canon( bf16( sum_{r=0..R-1} x[r][i,n] ) )   (fp32, r ascending)
+ * x is [R][M][N], the ranks' inputs.  Rows [row_begin, row_end) only.
+ * Returns 0 or -1. */
+int oracle_lamport_reduce(const uint16_t *x, uint16_t *t, int64_t M, int64_t N, int R,
+                          int64_t row_begin, int64_t row_end) {
+    if (M < 0 || N < 1 || R < 1 || row_begin < 0 || row_end > M || row_begin > row_end) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = row_begin; i < row_end; ++i) {
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int r = 0; r < R; ++r) acc = acc + bf16_to_f32(x[((int64_t)r * M + i) * N + n]);
+            const uint16_t b = f32_to_bf16_rne(acc);
+            t[i * N + n] = (b == LAMPORT_SENTINEL_BF16) ? 0u : b;
+        }
+    }
+    return 0;
+}
+
+/* Phase B is the one-slot consumer above applied to T: per row,
+ *     ms = (sum_n T^2) / N,  r = 1/sqrt(ms + eps),  out = bf16((T * r) * gamma)
+ * so the two-phase result differs from the one-shot one only by the bf16
+ * rounding of the sum before the norm. */
+int oracle_ar_rmsnorm_2phase(const uint16_t *x, const uint16_t *gamma, uint16_t *out, int64_t M,
+                             int64_t N, int R, float eps, int64_t row_begin, int64_t row_end) {
+    if (M < 0 || N < 1 || R < 1 || row_begin < 0 || row_end > M || row_begin > row_end) return -1;
+    const int64_t rows = row_end - row_begin;
+    uint16_t *t = (uint16_t *)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)N * sizeof(uint16_t));
+    if (!t) return -1;
+    /* T of the requested rows only, as a [rows, N] block */
+    int rc = 0;
+    for (int64_t i = 0; i < rows && rc == 0; ++i) {
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int r = 0; r < R; ++r) acc = acc + bf16_to_f32(x[((int64_t)r * M + row_begin + i) * N + n]);
+            const uint16_t b = f32_to_bf16_rne(acc);
+            t[i * N + n] = (b == LAMPORT_SENTINEL_BF16) ? 0u : b;
+        }
+    }
+    if (rows > 0) rc = oracle_ar_rmsnorm(t, gamma, out + row_begin * N, rows, N, 1, eps, 0, rows);
+    free(t);
+    return rc;
+}
+
 /* ---- weighted top-k combine ([P5] description: the intranode combine) -------
  *
  * x [T][E][H] bf16 (the E expert outputs of each token, contiguous per token),
