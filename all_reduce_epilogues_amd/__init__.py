@@ -73,6 +73,9 @@ def lib():
             "arepi_lamport_prefill": ([vp, i64, vp], i32),
             "arepi_lamport_publish": ([vp, vp, vp, i32, i64, i64, i32, i32, i32, vp], i32),
             "arepi_ar_rmsnorm_lamport": ([vp, vp, vp, i64, i64, i32, f32, i32, u32p, i64, vp], i32),
+            "arepi_ar_rmsnorm_lamport_2phase": ([vp, vp, vp, vp, i64, i64, i32, i32, f32, i32, u32p, i64, vp],
+                                                i32),
+            "arepi_emu_lamport_phase_a": ([vp, vp, i64, i64, i32, i32, i32, vp], i32),
             "arepi_combine_reduce": ([vp, vp, vp, i64, i32, i64, vp], i32),
             "arepi_combine_reduce_lds": ([vp, vp, vp, i64, i32, i64, vp], i32),
             "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp], i32),
@@ -313,6 +316,48 @@ def ar_rmsnorm_lamport(staging, gamma, out, eps: float = 1e-6, scope: int = SCOP
 
 
 # ---- combine --------------------------------------------------------------------------
+
+def _rank_arrays(inputs, staging):
+    R = len(inputs)
+    if len(staging) != R or R < 1:
+        raise ValueError("inputs and staging must list the same R >= 1 buffers")
+    shape = tuple(inputs[0].shape)
+    if len(shape) != 2:
+        raise ValueError("inputs are [M,N]")
+    ip = (ctypes.c_void_p * R)()
+    sp = (ctypes.c_void_p * R)()
+    for r in range(R):
+        _bf16(inputs[r], "inputs[%d]" % r, shape)
+        _bf16(staging[r], "staging[%d]" % r, shape)
+        ip[r] = inputs[r].data_ptr()
+        sp[r] = staging[r].data_ptr()
+    return R, shape, ip, sp
+
+
+def ar_rmsnorm_lamport_2phase(inputs, staging, gamma, out, rank: int, eps: float = 1e-6,
+                              scope: int = SCOPE_AGENT, status=None, spin_limit: int = 0, stream=None):
+    """Two-phase Lamport AR + RMSNorm on rank `rank`: reduce this rank's part of
+    the R inputs into every rank's staging (phase A), then consume this rank's
+    staging into out (phase B).  inputs/staging: lists of R bf16 [M,N] tensors
+    (staging armed with lamport_prefill)."""
+    R, (M, N), ip, sp = _rank_arrays(inputs, staging)
+    _bf16(gamma, "gamma", (N,))
+    _bf16(out, "out", (M, N))
+    if status is not None:
+        _flags(status, "status", (1,))
+    rc = lib().arepi_ar_rmsnorm_lamport_2phase(ctypes.cast(ip, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p),
+                                               _ptr(gamma), _ptr(out), M, N, R, rank, eps, scope, _ptr(status),
+                                               spin_limit, _stream(stream))
+    _check(rc, "ar_rmsnorm_lamport_2phase")
+
+
+def emu_lamport_phase_a(inputs, staging, rank: int, scope: int = SCOPE_AGENT, stream=None):
+    """Test-only: phase A of rank `rank` alone (stands in for a peer GPU)."""
+    R, (M, N), ip, sp = _rank_arrays(inputs, staging)
+    rc = lib().arepi_emu_lamport_phase_a(ctypes.cast(ip, ctypes.c_void_p), ctypes.cast(sp, ctypes.c_void_p),
+                                         M, N, R, rank, scope, _stream(stream))
+    _check(rc, "emu_lamport_phase_a")
+
 
 def combine_reduce(x, gate, out, stream=None, pipeline: str = "registers"):
     """out[t,h] = bf16(sum_k gate[t,k] * x[t,k,h]).  pipeline="lds" selects the

@@ -23,6 +23,7 @@
 // workgroup (wave shuffles, then LDS), and writes the normalised row.  (Two-
 // and eight-wave rows, persistent row loops and a slot-interleaved staging
 // layout all measured slower or equal on MI355X.)
+#include <algorithm>
 #include <string>
 
 #include "arepi_internal.h"
@@ -230,6 +231,190 @@ __global__ void __launch_bounds__(NT) ar_rmsnorm_kernel(uint16_t *__restrict__ s
     }
 }
 
+// ---- two-phase form (ROCm/aiter PR #4977, Approach: phase A is the
+// reduce-scatter with cross-device stores, phase B the consumer) ------------
+//
+// R ranks each hold a partial in[r] [M,N]; every rank has its own staging
+// [M,N] (armed with the sentinel).  The flattened tensor is cut into R parts
+// of ceil(P/R) 16-byte packs.  One launch on rank `rank`:
+//  Phase A: for each pack of part `rank`, add the R partials in fp32 (ranks
+//    ascending), round once to bf16, map -0.0 to +0.0 and store the pack into
+//    EVERY rank's staging (device-coherent 16-byte stores; no fence: the data
+//    is the flag).
+//  Phase B: each row of this rank's staging -- whose packs come from every
+//    rank's phase A -- is consumed as in the one-shot consumer with one slot:
+//    a plain load first, a coherent re-poll for packs still armed, re-arm of
+//    every pack consumed, then RMSNorm of the bf16 values into out.
+// Phase B of one block waits for phase A work of other blocks of the same
+// launch, so the launch is persistent: the grid is clamped to the workgroups
+// that can be resident at once, and every block finishes all of its phase A
+// work (which waits for nothing) before it polls.  Both phases are
+// grid-stride loops; phase A has no barriers, phase B's trip count is
+// block-uniform and each row ends with a barrier (the reduction slots are
+// reused by the next row).
+constexpr int kMaxRanks = 8;
+// Cache-policy operands of device-coherent 16-byte stores: sc1 (agent scope)
+// and sc0 sc1 (system scope), the bits the compiler gives the scoped relaxed
+// atomic stores of the same scope (checked against the emitted assembly).
+constexpr int kAuxCoherentAgent = 16;
+constexpr int kAuxCoherentSystem = 17;
+
+struct Lamport2Params {
+    const uint16_t *in[kMaxRanks];
+    uint16_t *stg[kMaxRanks];
+    const uint16_t *gamma;
+    uint16_t *out;
+    uint32_t *status;
+    int64_t M, N, spin_limit;
+    int R, rank, system, phase_b;
+    float eps;
+};
+
+template <int PPT, int NT>
+__global__ void __launch_bounds__(NT) lamport2_kernel(const Lamport2Params p) {
+    __shared__ float red[NT / 64];
+    const int tid = threadIdx.x;
+    const bool sys = p.system != 0;
+    const int64_t total = p.M * p.N / 8;  // 16-byte packs
+    const int64_t q = (total + p.R - 1) / p.R;
+    const int64_t a0 = min(total, q * p.rank), a1 = min(total, a0 + q);
+    const uint32_t plane2 = (uint32_t)(p.M * p.N * 2);
+
+    // ---- phase A ----
+    for (int64_t k = a0 + (int64_t)blockIdx.x * NT + tid; k < a1; k += (int64_t)gridDim.x * NT) {
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        uint4 v[kMaxRanks];
+#pragma unroll
+        for (int r = 0; r < kMaxRanks; ++r)
+            if (r < p.R) v[r] = load16_nt(p.in[r] + k * 8);
+#pragma unroll
+        for (int r = 0; r < kMaxRanks; ++r)
+            if (r < p.R) {
+                float f[8];
+                unpack8(v[r], f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = acc[e] + f[e];
+            }
+        const uint4 t = pack8(acc);
+        const i32x4 c = {(int)canon2(t.x), (int)canon2(t.y), (int)canon2(t.z), (int)canon2(t.w)};
+#pragma unroll
+        for (int d = 0; d < kMaxRanks; ++d)
+            if (d < p.R) {
+                const __amdgpu_buffer_rsrc_t rs =
+                    __builtin_amdgcn_make_buffer_rsrc((void *)p.stg[d], 0, (int)plane2, kBufferDword3);
+                if (sys)
+                    __builtin_amdgcn_raw_buffer_store_b128(c, rs, (uint32_t)(k * 16), 0, kAuxCoherentSystem);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b128(c, rs, (uint32_t)(k * 16), 0, kAuxCoherentAgent);
+            }
+    }
+    if (!p.phase_b) return;
+
+    // ---- phase B ----
+    const int packs = (int)(p.N / 8);
+    uint16_t *const mine = p.stg[p.rank];
+    const __amdgpu_buffer_rsrc_t st_rs = __builtin_amdgcn_make_buffer_rsrc((void *)mine, 0, (int)plane2, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t g_rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)p.gamma, 0, (int)(p.N * 2), kBufferDword3);
+    const __amdgpu_buffer_rsrc_t o_rs = __builtin_amdgcn_make_buffer_rsrc((void *)p.out, 0, (int)plane2, kBufferDword3);
+    const i32x4 armed = {(int)kSent2, (int)kSent2, (int)kSent2, (int)kSent2};
+    int64_t spins = 0;
+    bool gave_up = false;
+    for (int64_t row = blockIdx.x; row < p.M; row += gridDim.x) {
+        const uint32_t row2 = (uint32_t)(row * p.N * 2);
+        auto pack_off = [&](int j) {
+            const int pk = tid + j * NT;
+            return pk < packs ? row2 + (uint32_t)pk * 16u : kOob;
+        };
+        float s[PPT][8];
+        uint32_t bad = 0;
+        i32x4 qv[PPT];
+#pragma unroll
+        for (int j = 0; j < PPT; ++j)
+            qv[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(st_rs, pack_off(j), 0,
+                                                                                   kAuxNontemporal));
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const uint64_t lo = lo64(qv[j]), hi = hi64(qv[j]);
+            const bool b = has_sentinel(lo) | has_sentinel(hi);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[j][e] = 0.f;
+            add8(s[j], lo, hi);
+            bad |= (uint32_t)b << j;
+            __builtin_amdgcn_raw_buffer_store_b128(armed, st_rs, b ? kOob : pack_off(j), 0, kAuxNontemporal);
+        }
+        // slow pass: packs that had not landed, polled coherently
+        if (bad) {
+#pragma unroll
+            for (int j = 0; j < PPT; ++j) {
+                if (!((bad >> j) & 1u)) continue;
+                uint16_t *base = mine + row * p.N + (int64_t)(tid + j * NT) * 8;
+                uint64_t *p64 = reinterpret_cast<uint64_t *>(base);
+                uint64_t lo = load64_coherent(p64, sys), hi = load64_coherent(p64 + 1, sys);
+                while (!gave_up && (has_sentinel(lo) || has_sentinel(hi))) {
+                    if (++spins > p.spin_limit) {
+                        gave_up = true;
+                        if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                    lo = load64_coherent(p64, sys);
+                    hi = load64_coherent(p64 + 1, sys);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[j][e] = 0.f;
+                add8(s[j], lo, hi);
+                store16_nt(base, make_uint4(kSent2, kSent2, kSent2, kSent2));
+            }
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = ss + s[j][e] * s[j][e];
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+        if ((tid & 63) == 0) red[tid >> 6] = ss;
+        __syncthreads();
+        float tot = red[0];
+#pragma unroll
+        for (int w = 1; w < NT / 64; ++w) tot = tot + red[w];
+        const float r = 1.0f / sqrtf(tot / (float)p.N + p.eps);
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int pk = tid + j * NT;
+            const i32x4 g = __builtin_bit_cast(
+                i32x4, __builtin_amdgcn_raw_buffer_load_b128(g_rs, pk < packs ? (uint32_t)pk * 16u : kOob, 0, 0));
+            float gf[8], y[8];
+            unpack8(make_uint4((uint32_t)g[0], (uint32_t)g[1], (uint32_t)g[2], (uint32_t)g[3]), gf);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (s[j][e] * r) * gf[e];
+            const uint4 o = pack8(y);
+            const i32x4 ov = {(int)o.x, (int)o.y, (int)o.z, (int)o.w};
+            __builtin_amdgcn_raw_buffer_store_b128(ov, o_rs, pack_off(j), 0, kAuxNontemporal);
+        }
+        __syncthreads();  // red[] is rewritten by the next row
+    }
+}
+
+template <int PPT, int NT>
+int launch_lamport2(const Lamport2Params &p, hipStream_t s) {
+    // persistent grid: at most the workgroups resident at once
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lamport2_kernel<PPT, NT>, NT, 0) != hipSuccess ||
+        cus < 1 || per_cu < 1)
+        return fail(AREPI_ELAUNCH, "arepi_ar_rmsnorm_lamport_2phase: occupancy query failed");
+    const int64_t total = p.M * p.N / 8, q = (total + p.R - 1) / p.R;
+    int64_t want = std::max<int64_t>(p.phase_b ? p.M : 1, (q + NT - 1) / NT);
+    const int64_t grid = std::min<int64_t>(want, (int64_t)cus * per_cu);
+    hipLaunchKernelGGL((lamport2_kernel<PPT, NT>), dim3((unsigned)std::max<int64_t>(grid, 1)), dim3(NT), 0, s, p);
+    return check_launch("arepi_ar_rmsnorm_lamport_2phase");
+}
+
 }  // namespace
 }  // namespace arepi
 
@@ -306,4 +491,68 @@ extern "C" int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma
         AREPI_RMS_LAUNCH(8, 256);
 #undef AREPI_RMS_LAUNCH
     return check_launch("arepi_ar_rmsnorm_lamport");
+}
+
+// Shared validation of the two-phase entry points.
+static int lamport2_params(const char *who, const uint16_t *const *inputs, uint16_t *const *staging, int64_t M,
+                           int64_t N, int R, int rank, int scope, Lamport2Params &p) {
+    auto bad = [who](const std::string &m) { return fail(AREPI_EINVAL, std::string(who) + ": " + m); };
+    if (R < 1 || R > kMaxRanks) return bad("R=" + std::to_string(R) + " outside [1, 8]");
+    if (rank < 0 || rank >= R) return bad("rank=" + std::to_string(rank) + " outside [0, R-1]");
+    if (M < 0) return bad("M=" + std::to_string(M) + " must be >= 0");
+    if (N < 8 || N % 8) return bad("N=" + std::to_string(N) + " must be a positive multiple of 8");
+    if (N > 16384) return fail(AREPI_EUNSUPPORTED, std::string(who) + ": N=" + std::to_string(N) + " above 16384");
+    if (scope != AREPI_SCOPE_AGENT && scope != AREPI_SCOPE_SYSTEM) return bad("scope must be AGENT or SYSTEM");
+    if (M * N * 2 >= (int64_t)1 << 31)
+        return fail(AREPI_EUNSUPPORTED, std::string(who) + ": one [M,N] buffer must be below 2 GiB");
+    if (!inputs || !staging) return bad("inputs and staging must be host arrays of R device pointers");
+    for (int r = 0; r < R; ++r) {
+        if (!inputs[r] || !staging[r])
+            return bad("inputs[" + std::to_string(r) + "] and staging[" + std::to_string(r) + "] must be non-NULL");
+        if (!aligned16(inputs[r]) || !aligned16(staging[r])) return bad("buffers must be 16-byte aligned");
+        p.in[r] = inputs[r];
+        p.stg[r] = staging[r];
+    }
+    p.M = M;
+    p.N = N;
+    p.R = R;
+    p.rank = rank;
+    p.system = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
+    return AREPI_OK;
+}
+
+extern "C" int arepi_ar_rmsnorm_lamport_2phase(const uint16_t *const *inputs, uint16_t *const *staging,
+                                               const uint16_t *gamma, uint16_t *out, int64_t M, int64_t N, int R,
+                                               int rank, float eps, int scope, uint32_t *status,
+                                               int64_t spin_limit, arepi_stream_t stream) {
+    const char *who = "arepi_ar_rmsnorm_lamport_2phase";
+    Lamport2Params p{};
+    int rc = lamport2_params(who, inputs, staging, M, N, R, rank, scope, p);
+    if (rc) return rc;
+    if (!(eps >= 0.0f)) return fail(AREPI_EINVAL, std::string(who) + ": eps must be >= 0");
+    if (M == 0) return ok();
+    if (!gamma || !out || !aligned16(gamma) || !aligned16(out))
+        return fail(AREPI_EINVAL, std::string(who) + ": gamma and out must be non-NULL and 16-byte aligned");
+    p.gamma = gamma;
+    p.out = out;
+    p.status = status;
+    p.eps = eps;
+    p.spin_limit = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
+    p.phase_b = 1;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int64_t packs = N / 8;
+    if (packs <= 256) return launch_lamport2<1, 256>(p, s);
+    if (packs <= 512) return launch_lamport2<2, 256>(p, s);
+    if (packs <= 1024) return launch_lamport2<4, 256>(p, s);
+    return launch_lamport2<8, 256>(p, s);
+}
+
+extern "C" int arepi_emu_lamport_phase_a(const uint16_t *const *inputs, uint16_t *const *staging, int64_t M,
+                                         int64_t N, int R, int rank, int scope, arepi_stream_t stream) {
+    Lamport2Params p{};
+    int rc = lamport2_params("arepi_emu_lamport_phase_a", inputs, staging, M, N, R, rank, scope, p);
+    if (rc) return rc;
+    if (M == 0) return ok();
+    p.phase_b = 0;
+    return launch_lamport2<1, 256>(p, reinterpret_cast<hipStream_t>(stream));
 }

@@ -33,6 +33,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 LAMPORT_BYTES = 998_258_688 + 7168 * 2   # read 8P + write P + re-arm 8P (+ gamma)
 LAMPORT_BYTES_NO_REARM = 528_482_304 + 7168 * 2
 COMBINE_BYTES = 528_613_376              # read x + gate + write out
+# two-phase Lamport, one rank's call at [4096,7168]: phase A reads P and stores
+# P (its part into 8 stagings), phase B reads P, re-arms P, writes out P (+gamma)
+LAMPORT2_BYTES = 5 * 58_720_256 + 7168 * 2
 
 
 class _HipEvents:
@@ -86,7 +89,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sweep", action="store_true", help="also time the tp=8 sweep and the pre-staged tp=4 kernel")
     ap.add_argument("--only", default=None, choices=[None, "gemm_rs", "gemm_rs_prestaged", "gemm_rs_ring",
-                                                   "gemm_rs_ring_prestaged", "lamport", "combine"],
+                                                   "gemm_rs_ring_prestaged", "lamport", "lamport_2phase",
+                                                   "combine"],
                     help="run a single path (used for per-kernel profiles; counter collection serializes "
                          "kernels, so the GEMM's counters are taken pre-staged, without the producer stream)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -263,6 +267,43 @@ def lamport(A, inputs, torch, steps, warmup):
                 gbs_no_rearm_bytes=LAMPORT_BYTES_NO_REARM / ms / 1e6, S=S, M=M, N=N)
 
 
+def lamport_2phase(A, inputs, torch, steps, warmup):
+    """Two-phase Lamport AR + RMSNorm on rank 0 of 8, [4096,7168]: the seven
+    peers' phase A is emulated on a side stream after the previous call has
+    re-armed (their stores then wait in rank 0's staging); only the call itself
+    is timed: phase A of its own part (read P, store P across the 8 stagings)
+    and phase B (read P, re-arm P, write out P)."""
+    dev = torch.device("cuda:0")
+    case = inputs.lamport_case()
+    R, M, N = case["S"], case["M"], case["N"]
+    ins = [torch.from_numpy(case["src"][r].view("int16")).view(torch.bfloat16).to(dev) for r in range(R)]
+    gamma = torch.from_numpy(case["gamma"].view("int16")).view(torch.bfloat16).to(dev)
+    stg = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    for t in stg:
+        A.lamport_prefill(t)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    n = steps + warmup
+    es = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ee = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        side.wait_stream(main)
+        for d in range(1, R):
+            A.emu_lamport_phase_a(ins, stg, d, stream=side)
+        main.wait_stream(side)
+        es[i].record(main)
+        A.ar_rmsnorm_lamport_2phase(ins, stg, gamma, out, 0, case["eps"], status=status, stream=main)
+        ee[i].record(main)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("two-phase Lamport call timed out")
+    ms = sum(es[i].elapsed_time(ee[i]) for i in range(warmup, n)) / steps
+    return dict(ms=ms, gbs=LAMPORT2_BYTES / ms / 1e6, frac_hbm=LAMPORT2_BYTES / ms / 1e6 / PEAK_HBM_GBS,
+                R=R, M=M, N=N)
+
+
 def combine(A, inputs, torch, steps, warmup):
     dev = torch.device("cuda:0")
     case = inputs.combine_case()
@@ -361,6 +402,8 @@ def main():
         secondary["lamport_ar_rmsnorm"] = lamport(A, inputs, torch, max(10, a.steps // 2), 3)
     if a.only in (None, "combine"):
         secondary["combine_reduce"] = combine(A, inputs, torch, max(10, a.steps // 2), 3)
+    if a.only in (None, "lamport_2phase"):
+        secondary["lamport_2phase_ar_rmsnorm"] = lamport_2phase(A, inputs, torch, max(10, a.steps // 2), 3)
     if a.only in (None, "gemm_rs", "gemm_rs_prestaged"):
         secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2)
     if a.only in (None, "gemm_rs_ring"):

@@ -223,6 +223,32 @@ int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma, uint16_t 
                              int64_t N, int S, float eps, int scope, uint32_t *status,
                              int64_t spin_limit, arepi_stream_t stream);
 
+/* Two-phase form (same page, Approach: "phase A" is the reduce-scatter with
+ * cross-device stores, "phase B" the consumer; Correctness notes: every block
+ * finishes its producer work before it polls, and the grid is clamped to the
+ * workgroups that can be resident at once).  R ranks each hold a partial
+ * inputs[r] (bf16 [M,N]); every rank has a private staging[r] (bf16 [M,N],
+ * armed with arepi_lamport_prefill).  One call on rank `rank`:
+ *   phase A: the flattened tensor is cut into R parts of ceil(M*N/8/R) 16-byte
+ *     packs; for each pack of part `rank`, T = bf16(sum over r of inputs[r])
+ *     (fp32, ranks ascending, round-to-nearest-even), 0x8000 words mapped to
+ *     0x0000, stored into EVERY staging[d] with device-coherent stores at
+ *     `scope` (no fence: the data is the flag);
+ *   phase B: every pack of staging[rank] is waited for (it arrives from the
+ *     phase A of the rank owning its part), re-armed, and per row
+ *     out = bf16(T * (1/sqrt(mean(T^2) + eps)) * gamma).
+ * HOST arrays inputs/staging hold R device pointers.  staging[rank] is all
+ * 0x8000 again on return; the other ranks' staging receive part `rank`.
+ * Ordering between calls (a peer's phase A of the next call must not land
+ * before this call has re-armed) is the caller's: on one GPU stream order, or
+ * an event between the calls.  Constraints: 1 <= R <= 8, 0 <= rank < R,
+ * N % 8 == 0, 8 <= N <= 16384, M*N*2 < 2 GiB.  Waits are bounded by
+ * spin_limit (AREPI_STATUS_TIMEOUT in *status). */
+int arepi_ar_rmsnorm_lamport_2phase(const uint16_t *const *inputs, uint16_t *const *staging,
+                                    const uint16_t *gamma, uint16_t *out, int64_t M, int64_t N, int R,
+                                    int rank, float eps, int scope, uint32_t *status,
+                                    int64_t spin_limit, arepi_stream_t stream);
+
 /* ------------------------------------------------------------------------ *
  * Weighted top-k combine.
  *
@@ -261,6 +287,12 @@ int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, u
                             const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
                             int owner, int flag_tile_m, int flag_tile_n, int scope, int workgroups,
                             arepi_stream_t stream);
+
+/* Test-only: phase A of the two-phase Lamport call for rank `rank` alone
+ * (stands in for a peer GPU's phase A on one GPU).  Same arguments and
+ * constraints as arepi_ar_rmsnorm_lamport_2phase; never waits. */
+int arepi_emu_lamport_phase_a(const uint16_t *const *inputs, uint16_t *const *staging, int64_t M,
+                              int64_t N, int R, int rank, int scope, arepi_stream_t stream);
 
 #ifdef __cplusplus
 }
