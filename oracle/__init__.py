@@ -66,6 +66,10 @@ def _load():
     lib.oracle_ar_rmsnorm.argtypes = [vp, vp, vp, i64, i64, i32, f32, i64, i64]
     lib.oracle_ar_rmsnorm.restype = i32
     lib.oracle_combine.argtypes = [vp, vp, vp, i64, i32, i64, i64, i64]
+    lib.oracle_fp8_e4m3fn_to_f32.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_e4m3fn_to_f32.restype = ctypes.c_float
+    lib.oracle_gemm_rs_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i64, i64]
+    lib.oracle_gemm_rs_fp8.restype = i32
     lib.oracle_lamport_reduce.argtypes = [vp, vp, i64, i64, i32, i64, i64]
     lib.oracle_lamport_reduce.restype = i32
     lib.oracle_ar_rmsnorm_2phase.argtypes = [vp, vp, vp, i64, i64, i32, f32, i64, i64]
@@ -184,6 +188,49 @@ def gemm_rs_ring(x, w, upstream, R: int, owner: int, rows=None, want_send: bool 
                                      _p(send) if send is not None else None, M, N, K, R, owner, r0, r1)
     if rc != 0:
         raise ValueError("oracle_gemm_rs_ring rejected its arguments")
+    return out, send
+
+
+def fp8_e4m3fn_to_f32(code: int) -> float:
+    return float(_load().oracle_fp8_e4m3fn_to_f32(code))
+
+
+def gemm_rs_fp8(x, xs, wt, ws, recv, R: int, owner: int, rows=None, want_send: bool = True):
+    """fp8 block-scaled GEMM + reduce-scatter epilogue of one rank.
+
+    x: uint8 [M,K] e4m3fn; xs: float32 [M,K/128]; wt: uint8 [N,K] (W
+    transposed); ws: float32 [ceil(N/128),K/128]; recv as in gemm_rs()."""
+    x = np.ascontiguousarray(x, dtype=np.uint8)
+    wt = np.ascontiguousarray(wt, dtype=np.uint8)
+    xs = np.ascontiguousarray(xs, dtype=np.float32)
+    ws = np.ascontiguousarray(ws, dtype=np.float32)
+    M, K = x.shape
+    N, K2 = wt.shape
+    if K2 != K or K % 128:
+        raise ValueError("x is [M,K], wt is [N,K], K a multiple of 128")
+    if xs.shape != (M, K // 128) or ws.shape != ((N + 127) // 128, K // 128):
+        raise ValueError("xs must be [M,K/128] and ws [ceil(N/128),K/128]")
+    if M % R:
+        raise ValueError("M must be a multiple of R")
+    seg = M // R
+    keep = []
+    ptrs = (ctypes.c_void_p * R)()
+    for p in range(R):
+        if p == owner or R == 1:
+            ptrs[p] = None
+            continue
+        rp = _u16(recv[p])
+        if rp.shape != (seg, N):
+            raise ValueError("recv[%d] must be [%d,%d]" % (p, seg, N))
+        keep.append(rp)
+        ptrs[p] = rp.ctypes.data
+    out = np.zeros((seg, N), dtype=np.uint16)
+    send = np.zeros((M, N), dtype=np.uint16) if want_send else None
+    r0, r1 = (0, M) if rows is None else rows
+    rc = _load().oracle_gemm_rs_fp8(_p(x), _p(xs), _p(wt), _p(ws), ctypes.cast(ptrs, ctypes.c_void_p), _p(out),
+                                    _p(send) if send is not None else None, M, N, K, R, owner, r0, r1)
+    if rc != 0:
+        raise ValueError("oracle_gemm_rs_fp8 rejected its arguments")
     return out, send
 
 

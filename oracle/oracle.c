@@ -154,6 +154,62 @@ int oracle_gemm_rs(const uint16_t *x, const uint16_t *w, const uint16_t *const *
     return bad ? -1 : 0;
 }
 
+/* ---- fp8 block-scaled form of the local product ([P2] blockscale commit) ------
+ *
+ * Operands are fp8 e4m3fn bytes (the OCP encoding: sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent 0 is subnormal, S.1111.111 is NaN, no
+ * infinities; 0x38 is 1.0, largest finite 448).  X is quantised in 1x128
+ * blocks along K with fp32 scales xs [M][K/128] (row-major); W is held
+ * transposed, wt [N][K] (K contiguous), quantised in 128x128 blocks with fp32
+ * scales ws [ceil(N/128)][K/128].  The local product is the plain definition
+ *     C[m,n] = sum_{b} (xs[m,b] * ws[n/128,b]) * d_b[m,n],
+ *     d_b[m,n] = sum_{k in block b} dec(x[m,k]) * dec(wt[n,k])
+ * in fp32: k ascending inside a block (a product of two e4m3 values is exact
+ * in fp32), blocks ascending, the scale product formed first.  The
+ * reduce-scatter epilogue on C is that of oracle_gemm_rs. */
+float oracle_fp8_e4m3fn_to_f32(uint8_t b) {
+    const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    float v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexpf((float)m, -9); /* m/8 * 2^-6 */
+    else
+        v = ldexpf((float)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+int oracle_gemm_rs_fp8(const uint8_t *x, const float *xs, const uint8_t *wt, const float *ws,
+                       const uint16_t *const *recv, uint16_t *out, uint16_t *send, int64_t M, int64_t N,
+                       int64_t K, int R, int owner, int64_t row_begin, int64_t row_end) {
+    if (M < 0 || N < 0 || K < 0 || K % 128 || R < 1 || owner < 0 || owner >= R || M % R) return -1;
+    if (row_begin < 0 || row_end > M || row_begin > row_end) return -1;
+    const int64_t seg = M / R, KB = K / 128;
+    float lut[256];
+    for (int i = 0; i < 256; ++i) lut[i] = oracle_fp8_e4m3fn_to_f32((uint8_t)i);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = row_begin; i < row_end; ++i) {
+        const int64_t d = i / seg, li = i - d * seg;
+        for (int64_t n = 0; n < N; ++n) {
+            float acc = 0.0f;
+            for (int64_t b = 0; b < KB; ++b) {
+                float db = 0.0f;
+                for (int64_t k = b * 128; k < (b + 1) * 128; ++k) db = db + lut[x[i * K + k]] * lut[wt[n * K + k]];
+                const float s = xs[i * KB + b] * ws[(n / 128) * KB + b];
+                acc = acc + s * db;
+            }
+            if (d == owner) {
+                float t = acc;
+                for (int p = 0; p < R; ++p)
+                    if (p != owner) t = t + bf16_to_f32(recv[p][li * N + n]);
+                out[li * N + n] = f32_to_bf16_rne(t);
+            } else if (send) {
+                send[i * N + n] = f32_to_bf16_rne(acc);
+            }
+        }
+    }
+    return 0;
+}
+
 /* ---- push-ring form of the same reduce-scatter ([P1] description) ----------
  *
  * In the ring of [P1] each rank takes the running partial of a segment from
