@@ -70,6 +70,9 @@ def lib():
             "arepi_gemm_rs_ring_supports": ([i64, i64, i64, i32, i32, i32, i32, i32, i32], i32),
             "arepi_gemm_rs_ring": ([vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
                                     u32p, i64, vp], i32),
+            "arepi_gemm_rs_fp8_supports": ([i64, i64, i64, i32, i32, i32, i32, i32, i32], i32),
+            "arepi_gemm_rs_fp8": ([vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                   u32p, i64, vp], i32),
             "arepi_lamport_prefill": ([vp, i64, vp], i32),
             "arepi_lamport_publish": ([vp, vp, vp, i32, i64, i64, i32, i32, i32, vp], i32),
             "arepi_ar_rmsnorm_lamport": ([vp, vp, vp, i64, i64, i32, f32, i32, u32p, i64, vp], i32),
@@ -254,6 +257,58 @@ def gemm_rs_ring(x, w, upstream, ready_in, out, send, R: int, owner: int, ready_
                                   flag_tile_m, flag_tile_n, scope, tile, _ptr(status), spin_limit,
                                   _stream(stream))
     _check(rc, "gemm_rs_ring")
+
+
+def gemm_rs_fp8_supports(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publish=False, tile=0) -> int:
+    """0 when the fp8 block-scaled form supports the shape, else the negative status."""
+    return lib().arepi_gemm_rs_fp8_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish), tile)
+
+
+def gemm_rs_fp8(x, xs, wt, ws, recv, ready_in, out, R: int, owner: int, send=None, ready_out=None,
+                flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT, tile: int = 0,
+                status=None, spin_limit: int = 0, stream=None):
+    """fp8 e4m3fn block-scaled GEMM + reduce-scatter epilogue; see include/arepi.h.
+
+    x: torch.float8_e4m3fn (or uint8 bytes) [M,K]; xs: float32 [M,K/128];
+    wt: e4m3fn [N,K] (W transposed); ws: float32 [ceil(N/128),K/128]."""
+    torch = _torch()
+    fp8 = (torch.float8_e4m3fn, torch.uint8)
+    _need(x, "x", fp8)
+    _need(wt, "wt", fp8)
+    if x.dim() != 2 or wt.dim() != 2 or x.shape[1] != wt.shape[1]:
+        raise ValueError("x must be [M,K] and wt [N,K]")
+    M, K = x.shape
+    N = wt.shape[0]
+    if K % 128:
+        raise ValueError("K=%d must be a multiple of 128" % K)
+    _need(xs, "xs", (torch.float32,), (M, K // 128))
+    _need(ws, "ws", (torch.float32,), ((N + 127) // 128, K // 128))
+    if M % R:
+        raise ValueError("M=%d is not a multiple of R=%d" % (M, R))
+    seg = M // R
+    _bf16(out, "out", (seg, N))
+    if send is not None:
+        _bf16(send, "send", (M, N))
+    words = gemm_rs_flag_words(M, N, R, flag_tile_m, flag_tile_n)
+    if ready_in is not None:
+        _flags(ready_in, "ready_in", (R, words))
+    if ready_out is not None:
+        _flags(ready_out, "ready_out", (R, words))
+    if status is not None:
+        _flags(status, "status", (1,))
+    ptrs = (ctypes.c_void_p * R)()
+    if len(recv) != R:
+        raise ValueError("recv must list R=%d buffers (entry owner may be None)" % R)
+    for q in range(R):
+        if q == owner or recv[q] is None:
+            ptrs[q] = None
+            continue
+        _bf16(recv[q], "recv[%d]" % q, (seg, N))
+        ptrs[q] = recv[q].data_ptr()
+    rc = lib().arepi_gemm_rs_fp8(_ptr(x), _ptr(xs), _ptr(wt), _ptr(ws), ctypes.cast(ptrs, ctypes.c_void_p),
+                                 _ptr(ready_in), _ptr(out), _ptr(send), _ptr(ready_out), M, N, K, R, owner,
+                                 flag_tile_m, flag_tile_n, scope, tile, _ptr(status), spin_limit, _stream(stream))
+    _check(rc, "gemm_rs_fp8")
 
 
 def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N: int,

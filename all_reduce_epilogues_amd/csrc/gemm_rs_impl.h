@@ -87,6 +87,9 @@ struct GemmRsParams {
     // from the chain segment's last one (ob1), so the owner segment is last.
     const uint16_t *up[kMaxR];
     int ring, chain;
+    // fp8 block-scaled form only: x and w hold e4m3fn bytes, X [M,K] and W
+    // transposed [N,K]; xs [M][K/128] and ws [ceil(N/128)][K/128] fp32 scales
+    const float *xs, *ws;
 };
 
 
@@ -203,7 +206,7 @@ constexpr int lds_bytes() { return S * (BM * BK * 2 + BK * BN * 2); }
 // upstream partial of its own segment.
 enum { kNoOwnerRows = 0, kOwnerChunkA = 1, kOwnerRowsAnywhere = 2, kRing = 3 };
 
-template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, int KIND>
+template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, int KIND, bool FP8 = false>
 __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *smem, int rb, int cb, int64_t a0,
                                              int alen, int64_t b0, int blen) {
     constexpr int NWN = BN / WN;
@@ -453,6 +456,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     // t+1, overlapping its first operand reads.  Before that barrier every wave
     // has its own loads of step t+1 landed (vmcnt) and its LDS reads of stage
     // t%S done (the barrier's lgkmcnt wait).
+    if constexpr (!FP8) {
     Frag f[2];
 #pragma unroll
     for (int s0 = 0; s0 < S - 1; ++s0) issue_step(s0);
@@ -510,6 +514,149 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
             mma(f[(NK - 1) & 1]);
             interleave();
         }
+    }
+    } else {
+        // ---- fp8 e4m3fn block-scaled mainloop.  X [M,K] and W transposed
+        // [N,K] (both K-contiguous bytes); one 128-wide K block per step
+        // through two LDS stages of [BM][128] + [BN][128] bytes whose 16-byte
+        // chunks are XOR-swizzled by (row & 7).  Each block's product d_b is
+        // accumulated on v_mfma_f32_32x32x16_fp8_fp8 into the one accumulator
+        // set, which carries the running sum rescaled: after block b,
+        // acc *= s_b / s_{b+1} (s_b = xs[m,b] * ws[n/128,b]), and after the
+        // last block acc *= s_last, so acc ends at sum_b s_b * d_b.  The tile's
+        // columns lie in one 128-column scale block (BN == 128, n0 a multiple
+        // of 128).
+        static_assert(BN == 128, "one W scale block per tile");
+        constexpr int ROWB = 128;  // bytes of one tile row per step
+        constexpr int A8 = BM * ROWB, B8 = BN * ROWB, ST8 = A8 + B8;
+        static_assert(2 * ST8 <= LDS_BYTES, "two fp8 stages fit the stage memory");
+        constexpr int NTH = NW * 64;
+        constexpr int ACH = A8 / 16 / NTH, BCH = B8 / 16 / NTH;  // 16-byte chunks per thread per step
+        static_assert(ACH * NTH * 16 == A8 && BCH * NTH * 16 == B8, "fp8 tile split");
+        const int KB = (int)(K / 128);
+        const int nb = (int)(n0 / 128);
+        // byte offsets are 32-bit: M*K, N*K < 2^30 (host-checked)
+        const __amdgpu_buffer_rsrc_t x8r = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)(M * K), kBufferDword3);
+        const __amdgpu_buffer_rsrc_t w8r = __builtin_amdgcn_make_buffer_rsrc((void *)p.w, 0, (int)(N * K), kBufferDword3);
+        const __amdgpu_buffer_rsrc_t xsr =
+            __builtin_amdgcn_make_buffer_rsrc((void *)p.xs, 0, (int)(M * KB * 4), kBufferDword3);
+        uint32_t a_src[ACH], b_src[BCH];
+        int a_dst[ACH], b_dst[BCH];
+#pragma unroll
+        for (int i = 0; i < ACH; ++i) {
+            const int c = tid + i * NTH, v = c / 8, k16 = c % 8;
+            const int64_t gm = row_of(v);
+            a_src[i] = gm >= 0 ? (uint32_t)(gm * K + k16 * 16) : kOob;
+            a_dst[i] = v * ROWB + ((k16 ^ (v & 7)) << 4);
+        }
+#pragma unroll
+        for (int i = 0; i < BCH; ++i) {
+            const int c = tid + i * NTH, v = c / 8, k16 = c % 8;
+            const int64_t gn = n0 + v;
+            b_src[i] = gn < N ? (uint32_t)(gn * K + k16 * 16) : kOob;
+            b_dst[i] = A8 + v * ROWB + ((k16 ^ (v & 7)) << 4);
+        }
+        i32x4 ra[ACH], rb[BCH];
+        auto gload = [&](int b) {
+            const uint32_t kb = (uint32_t)b * 128u;
+#pragma unroll
+            for (int i = 0; i < ACH; ++i)
+                ra[i] = __builtin_bit_cast(
+                    i32x4, __builtin_amdgcn_raw_buffer_load_b128(x8r, a_src[i] == kOob ? kOob : a_src[i] + kb, 0, 0));
+#pragma unroll
+            for (int i = 0; i < BCH; ++i)
+                rb[i] = __builtin_bit_cast(
+                    i32x4, __builtin_amdgcn_raw_buffer_load_b128(w8r, b_src[i] == kOob ? kOob : b_src[i] + kb, 0, 0));
+        };
+        auto lstore = [&](int stage) {
+            lds_t *base = S0 + stage * ST8;
+#pragma unroll
+            for (int i = 0; i < ACH; ++i) *(__attribute__((address_space(3))) i32x4 *)(base + a_dst[i]) = ra[i];
+#pragma unroll
+            for (int i = 0; i < BCH; ++i) *(__attribute__((address_space(3))) i32x4 *)(base + b_dst[i]) = rb[i];
+        };
+        // scale offsets of this lane's accumulator rows (row 8*(r/4) + 4*(lane/32) + r%4 of MFMA tile i)
+        uint32_t s_off[TM][16];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int v = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int64_t gm = row_of(v);
+                s_off[i][r] = gm >= 0 ? (uint32_t)(gm * KB * 4) : kOob;
+            }
+        // row scales of block b; rows past the end get 1 (their data is zero)
+        auto load_scales = [&](int b, float (&sc)[TM][16]) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                        xsr, s_off[i][r] == kOob ? kOob : s_off[i][r] + (uint32_t)b * 4u, 0, 0));
+                    sc[i][r] = s_off[i][r] == kOob ? 1.0f : v;
+                }
+        };
+        float scur[TM][16], snext[TM][16];
+        gload(0);
+        load_scales(0, scur);
+        float sbc = p.ws[(int64_t)nb * KB];
+        lstore(0);
+        __syncthreads();
+        for (int b = 0; b < KB; ++b) {
+            const bool more = b + 1 < KB;
+            float sbn = 1.0f;
+            if (more) {
+                gload(b + 1);
+                load_scales(b + 1, snext);
+                sbn = p.ws[(int64_t)nb * KB + b + 1];
+            }
+            const lds_t *As = S0 + (b & 1) * ST8;
+            const lds_t *Bs = As + A8;
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) {
+                long av[TM], bv[TN];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int v = wm * WM + i * 32 + (lane & 31);
+                    av[i] = *(const __attribute__((address_space(3))) long *)(As + v * ROWB + ((s8 ^ (v & 7)) << 4) +
+                                                                             8 * (lane >> 5));
+                }
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int v = wn * WN + j * 32 + (lane & 31);
+                    bv[j] = *(const __attribute__((address_space(3))) long *)(Bs + v * ROWB + ((s8 ^ (v & 7)) << 4) +
+                                                                             8 * (lane >> 5));
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av[i], bv[j], acc[i][j], 0, 0, 0);
+            }
+            if (more) {
+                const float cs = sbc / sbn;
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float f = (scur[i][r] / snext[i][r]) * cs;
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) acc[i][j][r] *= f;
+                        scur[i][r] = snext[i][r];
+                    }
+                sbc = sbn;
+                lstore((b + 1) & 1);  // free since the barrier that ended step b-1
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float f = scur[i][r] * sbc;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j][r] *= f;
+            }
     }
     wait_vmcnt_zero();
     __syncthreads();  // the stages are reused by the epilogue below

@@ -82,6 +82,29 @@ def gemm_rs_ring_case(M: int, N: int, K: int, R: int, owner: int = 0, seed: int 
     return c
 
 
+def fp8_e4m3fn_codes(shape, std: float, g: torch.Generator) -> np.ndarray:
+    """e4m3fn bytes of N(0, std) samples (torch's round-to-nearest conversion)."""
+    t = torch.randn(*shape, generator=g, dtype=torch.float32) * std
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def gemm_rs_fp8_case(M: int, N: int, K: int, R: int, owner: int = 0, seed: int = 1002,
+                     x_std: float = 2.0, w_std: float = 2.0, recv_std: float = 0.5) -> dict:
+    """fp8 operands of the block-scaled GEMM + reduce-scatter: x [M,K] and wt
+    [N,K] e4m3fn bytes, positive fp32 block scales xs [M,K/128] and ws
+    [ceil(N/128),K/128] ~ U(0.02, 0.06), and the R-1 bf16 peer partials."""
+    if M % R or K % 128:
+        raise ValueError("M must be a multiple of R and K of 128")
+    g = _gen(seed)
+    seg = M // R
+    x = fp8_e4m3fn_codes((M, K), x_std, g)
+    wt = fp8_e4m3fn_codes((N, K), w_std, g)
+    xs = (0.02 + 0.04 * torch.rand(M, K // 128, generator=g)).numpy().astype(np.float32)
+    ws = (0.02 + 0.04 * torch.rand((N + 127) // 128, K // 128, generator=g)).numpy().astype(np.float32)
+    recv = [None if p == owner else normal_bf16((seg, N), recv_std, g) for p in range(R)]
+    return dict(x=x, xs=xs, wt=wt, ws=ws, recv=recv, M=M, N=N, K=K, R=R, owner=owner, seed=seed)
+
+
 WORKLOADS = {
     1: dict(M=256, N=512, K=256, R=2, dist="uniform"),
     2: dict(M=4096, N=4096, K=2048, R=4, dist="normal"),

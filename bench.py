@@ -29,6 +29,7 @@ import time
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 
 LAMPORT_BYTES = 998_258_688 + 7168 * 2   # read 8P + write P + re-arm 8P (+ gamma)
 LAMPORT_BYTES_NO_REARM = 528_482_304 + 7168 * 2
@@ -89,7 +90,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sweep", action="store_true", help="also time the tp=8 sweep and the pre-staged tp=4 kernel")
     ap.add_argument("--only", default=None, choices=[None, "gemm_rs", "gemm_rs_prestaged", "gemm_rs_ring",
-                                                   "gemm_rs_ring_prestaged", "lamport", "lamport_2phase",
+                                                   "gemm_rs_ring_prestaged", "gemm_rs_fp8", "lamport", "lamport_2phase",
                                                    "combine"],
                     help="run a single path (used for per-kernel profiles; counter collection serializes "
                          "kernels, so the GEMM's counters are taken pre-staged, without the producer stream)")
@@ -267,6 +268,51 @@ def lamport(A, inputs, torch, steps, warmup):
                 gbs_no_rearm_bytes=LAMPORT_BYTES_NO_REARM / ms / 1e6, S=S, M=M, N=N)
 
 
+def gemm_rs_fp8_prestaged(A, inputs, torch, steps, warmup):
+    """fp8 e4m3fn block-scaled GEMM + reduce-scatter epilogue on the tp=4 share
+    (X [4096,2048], W^T [4096,2048], 1x128 / 128x128 fp32 scales, R=4), peer
+    partials landed beforehand: the kernel alone."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    M, N, K, R, owner = 4096, 4096, 2048, 4, 0
+    case = inputs.gemm_rs_fp8_case(M, N, K, R, owner=owner, seed=1002)
+    seg = M // R
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x, wt, xs, ws = u8(case["x"]), u8(case["wt"]), u8(case["xs"]), u8(case["ws"])
+    recv = [None if q == owner else torch.from_numpy(case["recv"][q].view("int16")).view(torch.bfloat16).to(dev)
+            for q in range(R)]
+    words = A.gemm_rs_flag_words(M, N, R)
+    tiles = ((seg + 127) // 128) * ((N + 127) // 128)
+    full = np.zeros((R, words), np.uint32)
+    for q in range(R):
+        if q != owner:
+            for t in range(tiles):
+                full[q, t // 32] |= np.uint32(1 << (t % 32))
+    rin = torch.from_numpy(full.view(np.int32)).to(dev)
+    rout = torch.zeros((R, words), dtype=torch.int32, device=dev)
+    out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
+    send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def call():
+        A.gemm_rs_fp8(x, xs, wt, ws, recv, rin, out, R, owner, send=send, ready_out=rout)
+
+    for _ in range(warmup):
+        call()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        call()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    flops = 2.0 * M * N * K
+    byts = M * K + N * K + 4.0 * (M + N // 128) * (K // 128) + 2.0 * ((R - 1) * seg * N + seg * N + (M - seg) * N)
+    return dict(M=M, N=N, K=K, R=R, tile="128x128", ms=ms, tflops=flops / ms / 1e9,
+                frac_mfma_fp8=flops / ms / 1e9 / PEAK_FP8_TFLOPS, gbs=byts / ms / 1e6,
+                frac_hbm=byts / ms / 1e6 / PEAK_HBM_GBS)
+
+
 def lamport_2phase(A, inputs, torch, steps, warmup):
     """Two-phase Lamport AR + RMSNorm on rank 0 of 8, [4096,7168]: the seven
     peers' phase A is emulated on a side stream after the previous call has
@@ -411,6 +457,8 @@ def main():
         secondary["gemm_rs_ring_tp4_step"] = dict(ms_per_step=r["ms_per_step"], tflops=r["tflops"],
                                                   kernel_ms=r["gemm_ms"], kernel_tflops=r["gemm_tflops"],
                                                   frac_mfma=r["gemm_tflops"] / PEAK_BF16_TFLOPS, tile=r["tile"])
+    if a.only in (None, "gemm_rs_fp8"):
+        secondary["gemm_rs_fp8_tp4_prestaged"] = gemm_rs_fp8_prestaged(A, inputs, torch, a.steps, a.warmup)
     if a.only in (None, "gemm_rs_ring", "gemm_rs_ring_prestaged"):
         secondary["gemm_rs_ring_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2,
                                                                     ring=True)

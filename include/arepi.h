@@ -190,6 +190,34 @@ int arepi_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const uint16_t *con
                        int64_t spin_limit, arepi_stream_t stream);
 
 /* ------------------------------------------------------------------------ *
+ * GEMM + reduce-scatter epilogue, fp8 block-scaled local product.
+ *
+ * Defined by ROCm/mori PR #662, the blockscale commit (X quantised 1x128 along
+ * K, W 128x128, fp32 scales; the scales vary along K, so the local product is
+ * sum over K blocks b of xs[m,b] * ws[n/128,b] * d_b with d_b the fp8 product
+ * of block b; applied with the running rescale t_b = t_{b-1}*(s_{b-1}/s_b) +
+ * d_b, out = t_last * s_last), and by its re-review finding that the gfx950
+ * matrix atom reads OCP e4m3fn bytes.
+ *   x   e4m3fn bytes [M,K]            X_r
+ *   xs  fp32 [M][K/128]               row-major; must be > 0 and finite
+ *   wt  e4m3fn bytes [N,K]            W_r TRANSPOSED (K contiguous)
+ *   ws  fp32 [ceil(N/128)][K/128]     row-major; must be > 0 and finite
+ * The reduce-scatter epilogue and every other argument are those of
+ * arepi_gemm_rs_fused (direct sum over the R-1 peers).  The compute tile is
+ * 128x128 (tile_cfg may only carry AREPI_TILE_CONSUME_READY).  Constraints:
+ * those of arepi_gemm_rs_fused plus K % 128 == 0; xs 4-byte aligned.
+ * e4m3fnuz bytes are not this encoding (the same bits decode to other values).
+ * ------------------------------------------------------------------------ */
+int arepi_gemm_rs_fp8_supports(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
+                               int flag_tile_n, int publish, int tile_cfg);
+
+int arepi_gemm_rs_fp8(const uint8_t *x, const float *xs, const uint8_t *wt, const float *ws,
+                      const uint16_t *const *recv, uint32_t *ready_in, uint16_t *out, uint16_t *send,
+                      uint32_t *ready_out, int64_t M, int64_t N, int64_t K, int R, int owner,
+                      int flag_tile_m, int flag_tile_n, int scope, int tile_cfg, uint32_t *status,
+                      int64_t spin_limit, arepi_stream_t stream);
+
+/* ------------------------------------------------------------------------ *
  * Lamport all-reduce + RMSNorm.
  *
  * Defined by ROCm/aiter PR #4977 "[HIP] Single-kernel Lamport fused all-reduce
