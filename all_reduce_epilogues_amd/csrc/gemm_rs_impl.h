@@ -525,7 +525,8 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         // acc *= s_b / s_{b+1} (s_b = xs[m,b] * ws[n/128,b]), and after the
         // last block acc *= s_last, so acc ends at sum_b s_b * d_b.  The tile's
         // columns lie in one 128-column scale block (BN == 128, n0 a multiple
-        // of 128).
+        // of 128).  The kernel allocates 2*BM floats of LDS past the stages
+        // for the per-row factors.
         static_assert(BN == 128, "one W scale block per tile");
         constexpr int ROWB = 128;  // bytes of one tile row per step
         constexpr int A8 = BM * ROWB, B8 = BN * ROWB, ST8 = A8 + B8;
@@ -538,8 +539,6 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         // byte offsets are 32-bit: M*K, N*K < 2^30 (host-checked)
         const __amdgpu_buffer_rsrc_t x8r = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)(M * K), kBufferDword3);
         const __amdgpu_buffer_rsrc_t w8r = __builtin_amdgcn_make_buffer_rsrc((void *)p.w, 0, (int)(N * K), kBufferDword3);
-        const __amdgpu_buffer_rsrc_t xsr =
-            __builtin_amdgcn_make_buffer_rsrc((void *)p.xs, 0, (int)(M * KB * 4), kBufferDword3);
         uint32_t a_src[ACH], b_src[BCH];
         int a_dst[ACH], b_dst[BCH];
 #pragma unroll
@@ -575,41 +574,48 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
 #pragma unroll
             for (int i = 0; i < BCH; ++i) *(__attribute__((address_space(3))) i32x4 *)(base + b_dst[i]) = rb[i];
         };
-        // scale offsets of this lane's accumulator rows (row 8*(r/4) + 4*(lane/32) + r%4 of MFMA tile i)
-        uint32_t s_off[TM][16];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int v = wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                const int64_t gm = row_of(v);
-                s_off[i][r] = gm >= 0 ? (uint32_t)(gm * KB * 4) : kOob;
+        // Per-row factors through LDS (past the stages; the kernel allocates
+        // them): before step b's barrier, threads t < BM write for tile row t
+        // the factor applied after block b, s_b/s_{b+1} (or s_last after the
+        // last block), into buffer b&1; after the barrier every lane reads the
+        // factors of its own accumulator rows.  One division per row and block
+        // instead of one per lane.  Rows past the end get factor 1 (their
+        // products are zero).
+        float *const fac = reinterpret_cast<float *>(smem + LDS_BYTES);  // [2][BM]
+        const int64_t frow = tid < BM ? row_of(tid) : -1;
+        auto row_scale = [&](int b) -> float {
+            return frow >= 0 ? p.xs[frow * KB + b] : 1.0f;
+        };
+        auto col_scale = [&](int b) -> float { return p.ws[(int64_t)nb * KB + b]; };
+        // factor of this thread's row after block b
+        auto write_factor = [&](int b) {
+            if (tid < BM) {
+                float f;
+                if (b + 1 < KB)
+                    f = (row_scale(b) / row_scale(b + 1)) * (col_scale(b) / col_scale(b + 1));
+                else
+                    f = row_scale(b) * col_scale(b);
+                fac[(b & 1) * BM + tid] = f;
             }
-        // row scales of block b; rows past the end get 1 (their data is zero)
-        auto load_scales = [&](int b, float (&sc)[TM][16]) {
+        };
+        auto apply_factor = [&](int b) {
+            const float *fb = fac + (b & 1) * BM;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float v = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                        xsr, s_off[i][r] == kOob ? kOob : s_off[i][r] + (uint32_t)b * 4u, 0, 0));
-                    sc[i][r] = s_off[i][r] == kOob ? 1.0f : v;
+                    const float f = fb[wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3)];
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) acc[i][j][r] *= f;
                 }
         };
-        float scur[TM][16], snext[TM][16];
         gload(0);
-        load_scales(0, scur);
-        float sbc = p.ws[(int64_t)nb * KB];
         lstore(0);
+        write_factor(0);
         __syncthreads();
         for (int b = 0; b < KB; ++b) {
             const bool more = b + 1 < KB;
-            float sbn = 1.0f;
-            if (more) {
-                gload(b + 1);
-                load_scales(b + 1, snext);
-                sbn = p.ws[(int64_t)nb * KB + b + 1];
-            }
+            if (more) gload(b + 1);
             const lds_t *As = S0 + (b & 1) * ST8;
             const lds_t *Bs = As + A8;
 #pragma unroll
@@ -633,30 +639,15 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                     for (int j = 0; j < TN; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av[i], bv[j], acc[i][j], 0, 0, 0);
             }
+            // after block b: acc *= s_b / s_{b+1} (s_last after the last block);
+            // the factors were written before the barrier that ended step b-1
+            apply_factor(b);
             if (more) {
-                const float cs = sbc / sbn;
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float f = (scur[i][r] / snext[i][r]) * cs;
-#pragma unroll
-                        for (int j = 0; j < TN; ++j) acc[i][j][r] *= f;
-                        scur[i][r] = snext[i][r];
-                    }
-                sbc = sbn;
                 lstore((b + 1) & 1);  // free since the barrier that ended step b-1
+                write_factor(b + 1);  // buffer (b+1)&1: last read in step b-1
             }
             __syncthreads();
         }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float f = scur[i][r] * sbc;
-#pragma unroll
-                for (int j = 0; j < TN; ++j) acc[i][j][r] *= f;
-            }
     }
     wait_vmcnt_zero();
     __syncthreads();  // the stages are reused by the epilogue below
