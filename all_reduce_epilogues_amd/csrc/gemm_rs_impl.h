@@ -519,7 +519,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         // ---- fp8 e4m3fn block-scaled mainloop.  X [M,K] and W transposed
         // [N,K] (both K-contiguous bytes); one 128-wide K block per step
         // through two LDS stages of [BM][128] + [BN][128] bytes whose 16-byte
-        // chunks are XOR-swizzled by (row & 7).  Each block's product d_b is
+        // chunks are XOR-swizzled by row.  Each block's product d_b is
         // accumulated on v_mfma_f32_32x32x16_fp8_fp8 into the one accumulator
         // set, which carries the running sum rescaled: after block b,
         // acc *= s_b / s_{b+1} (s_b = xs[m,b] * ws[n/128,b]), and after the
@@ -528,6 +528,11 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         // of 128).  The kernel allocates 2*BM floats of LDS past the stages
         // for the per-row factors.
         static_assert(BN == 128, "one W scale block per tile");
+        // Chunk c of tile row v sits at c ^ swz8(v).  Two 128-byte rows share a
+        // 256-byte line of the 64 banks; ((v >> 1) & 7) sends the 16 rows of
+        // one parity to 8 positions twice each, so the 8-byte operand reads of
+        // 32 consecutive rows take the minimum two passes.
+        auto swz8 = [](int v) { return (v >> 1) & 7; };
         constexpr int ROWB = 128;  // bytes of one tile row per step
         constexpr int A8 = BM * ROWB, B8 = BN * ROWB, ST8 = A8 + B8;
         static_assert(2 * ST8 <= LDS_BYTES, "two fp8 stages fit the stage memory");
@@ -546,14 +551,14 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
             const int c = tid + i * NTH, v = c / 8, k16 = c % 8;
             const int64_t gm = row_of(v);
             a_src[i] = gm >= 0 ? (uint32_t)(gm * K + k16 * 16) : kOob;
-            a_dst[i] = v * ROWB + ((k16 ^ (v & 7)) << 4);
+            a_dst[i] = v * ROWB + ((k16 ^ swz8(v)) << 4);
         }
 #pragma unroll
         for (int i = 0; i < BCH; ++i) {
             const int c = tid + i * NTH, v = c / 8, k16 = c % 8;
             const int64_t gn = n0 + v;
             b_src[i] = gn < N ? (uint32_t)(gn * K + k16 * 16) : kOob;
-            b_dst[i] = A8 + v * ROWB + ((k16 ^ (v & 7)) << 4);
+            b_dst[i] = A8 + v * ROWB + ((k16 ^ swz8(v)) << 4);
         }
         i32x4 ra[ACH], rb[BCH];
         auto gload = [&](int b) {
@@ -624,13 +629,13 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     const int v = wm * WM + i * 32 + (lane & 31);
-                    av[i] = *(const __attribute__((address_space(3))) long *)(As + v * ROWB + ((s8 ^ (v & 7)) << 4) +
+                    av[i] = *(const __attribute__((address_space(3))) long *)(As + v * ROWB + ((s8 ^ swz8(v)) << 4) +
                                                                              8 * (lane >> 5));
                 }
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int v = wn * WN + j * 32 + (lane & 31);
-                    bv[j] = *(const __attribute__((address_space(3))) long *)(Bs + v * ROWB + ((s8 ^ (v & 7)) << 4) +
+                    bv[j] = *(const __attribute__((address_space(3))) long *)(Bs + v * ROWB + ((s8 ^ swz8(v)) << 4) +
                                                                              8 * (lane >> 5));
                 }
 #pragma unroll
