@@ -251,19 +251,22 @@ def lamport(A, inputs, torch, steps, warmup):
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     n = steps + warmup
-    es = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    ee = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    # fence-free HIP events on the consumer's stream, as for the GEMM
+    H = _HipEvents()
+    es = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n)]
+    ee = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n)]
     for i in range(n):
         side.wait_stream(main)   # publish only into re-armed staging
         A.lamport_publish(src, st, order, stream=side)
         main.wait_stream(side)
-        es[i].record(main)
+        H.record(es[i], main)
         A.ar_rmsnorm_lamport(st, gamma, out, case["eps"], status=status, stream=main)
-        ee[i].record(main)
+        H.record(ee[i], main)
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError("Lamport consumer timed out")
-    ms = sum(es[i].elapsed_time(ee[i]) for i in range(warmup, n)) / steps
+    ms = sum(H.elapsed_ms(es[i], ee[i]) for i in range(warmup, n)) / steps
+    H.destroy(es + ee)
     return dict(ms=ms, gbs=LAMPORT_BYTES / ms / 1e6, frac_hbm=LAMPORT_BYTES / ms / 1e6 / PEAK_HBM_GBS,
                 gbs_no_rearm_bytes=LAMPORT_BYTES_NO_REARM / ms / 1e6, S=S, M=M, N=N)
 
@@ -332,20 +335,23 @@ def lamport_2phase(A, inputs, torch, steps, warmup):
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     n = steps + warmup
-    es = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-    ee = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    # fence-free HIP events on the consumer's stream, as for the GEMM
+    H = _HipEvents()
+    es = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n)]
+    ee = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n)]
     for i in range(n):
         side.wait_stream(main)
         for d in range(1, R):
             A.emu_lamport_phase_a(ins, stg, d, stream=side)
         main.wait_stream(side)
-        es[i].record(main)
+        H.record(es[i], main)
         A.ar_rmsnorm_lamport_2phase(ins, stg, gamma, out, 0, case["eps"], status=status, stream=main)
-        ee[i].record(main)
+        H.record(ee[i], main)
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError("two-phase Lamport call timed out")
-    ms = sum(es[i].elapsed_time(ee[i]) for i in range(warmup, n)) / steps
+    ms = sum(H.elapsed_ms(es[i], ee[i]) for i in range(warmup, n)) / steps
+    H.destroy(es + ee)
     return dict(ms=ms, gbs=LAMPORT2_BYTES / ms / 1e6, frac_hbm=LAMPORT2_BYTES / ms / 1e6 / PEAK_HBM_GBS,
                 R=R, M=M, N=N)
 
