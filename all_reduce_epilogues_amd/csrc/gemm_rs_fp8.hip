@@ -8,15 +8,15 @@
 // finding that the gfx950 matrix atom reads the OCP e4m3fn encoding (e4m3fnuz
 // bytes are not accepted).  The reduce-scatter epilogue is the direct-sum form
 // of gemm_rs.hip; the mainloop is the fp8 branch of the shared body
-// (gemm_rs_impl.h), on a 128x128 tile of eight 64x32 waves (two per SIMD: one
-// wave's MFMAs run while the other waits on its loads).
+// (gemm_rs_impl.h), on a 128x128 tile of four 64x64 waves, two workgroups per
+// CU (per MFMA a 64x64 wave reads half the LDS bytes a 64x32 wave does).
 #include "gemm_rs_impl.h"
 
 namespace arepi {
 namespace {
 
 template <int PEERS>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_rs_fp8_kernel(const GemmRsParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_rs_fp8_kernel(const GemmRsParams p) {
     // the stages, then 2 x 128 per-row scale factors of the fp8 mainloop
     __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<128, 128, 64, 2>() + 2 * 128 * 4];
     constexpr int BM = 128, CK = 64;
@@ -29,9 +29,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool own_a = alen > 0 && a0 < oseg1 && a0 + alen > oseg0;
     const bool own_b = blen > 0 && b0 < oseg1 && b0 + blen > oseg0;
     if (!own_a && !own_b)
-        gemm_rs_body<128, 128, 64, 32, 64, 2, 2, PEERS, kNoOwnerRows, true>(p, smem, rb, cb, a0, alen, b0, blen);
+        gemm_rs_body<128, 128, 64, 64, 64, 2, 2, PEERS, kNoOwnerRows, true>(p, smem, rb, cb, a0, alen, b0, blen);
     else
-        gemm_rs_body<128, 128, 64, 32, 64, 2, 2, PEERS, kOwnerRowsAnywhere, true>(p, smem, rb, cb, a0, alen, b0,
+        gemm_rs_body<128, 128, 64, 64, 64, 2, 2, PEERS, kOwnerRowsAnywhere, true>(p, smem, rb, cb, a0, alen, b0,
                                                                                  blen);
 }
 
@@ -103,10 +103,10 @@ extern "C" int arepi_gemm_rs_fp8(const uint8_t *x, const float *xs, const uint8_
     if (rc) return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p.npeers <= 1)
-        hipLaunchKernelGGL(gemm_rs_fp8_kernel<1>, dim3(p.nWG), dim3(512), 0, s, p);
+        hipLaunchKernelGGL(gemm_rs_fp8_kernel<1>, dim3(p.nWG), dim3(256), 0, s, p);
     else if (p.npeers <= 3)
-        hipLaunchKernelGGL(gemm_rs_fp8_kernel<3>, dim3(p.nWG), dim3(512), 0, s, p);
+        hipLaunchKernelGGL(gemm_rs_fp8_kernel<3>, dim3(p.nWG), dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL(gemm_rs_fp8_kernel<kMaxR - 1>, dim3(p.nWG), dim3(512), 0, s, p);
+        hipLaunchKernelGGL(gemm_rs_fp8_kernel<kMaxR - 1>, dim3(p.nWG), dim3(256), 0, s, p);
     return check_launch("arepi_gemm_rs_fp8");
 }
