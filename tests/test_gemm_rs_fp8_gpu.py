@@ -141,3 +141,14 @@ def test_tp4_share_prestaged_and_concurrent_producer():
     assert int(status.item()) == 0
     assert np.array_equal(conc["out"], pre["out"]) and np.array_equal(conc["send"], pre["send"])
     assert not from_dev_u32(rin).any(), "consumed bits must be cleared"
+
+
+@pytest.mark.parametrize("M,owner", [(256, 0), (1024, 6)])
+def test_tp8_shapes(M, owner):
+    """The tp=8 wide shape (N=7168, K=2048, eight ranks) in the fp8 form."""
+    case = inputs.gemm_rs_fp8_case(M, 7168, 2048, 8, owner=owner, seed=1003)
+    R, seg = 8, M // 8
+    res = run(case)
+    rows = [(owner * seg, (owner + 1) * seg)]
+    rows += [(d * seg, d * seg + min(8, seg)) for d in range(R) if d != owner]
+    check(case, res, rows=rows, what="fp8 tp8 M=%d" % M)
