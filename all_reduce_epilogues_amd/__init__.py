@@ -81,7 +81,8 @@ def lib():
             "arepi_emu_lamport_phase_a": ([vp, vp, i64, i64, i32, i32, i32, vp], i32),
             "arepi_combine_reduce": ([vp, vp, vp, i64, i32, i64, vp], i32),
             "arepi_combine_reduce_lds": ([vp, vp, vp, i64, i32, i64, vp], i32),
-            "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp], i32),
+            "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp],
+                                        i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -313,9 +314,10 @@ def gemm_rs_fp8(x, xs, wt, ws, recv, ready_in, out, R: int, owner: int, send=Non
 
 def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N: int,
                       flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT,
-                      workgroups: int = 0, stream=None):
-    """Test-only: land (peer, tile) items of src[p] into recv[p] and set their bits
-    (workgroups > 0: that many items in flight at a time)."""
+                      workgroups: int = 0, items_per_release: int = 1, stream=None):
+    """Test-only: land (peer, tile) items of src[p] into recv[p] and set their bits,
+    items_per_release tiles per release (workgroups > 0: that many batches in
+    flight at a time)."""
     seg = M // R
     torch = _torch()
     _need(order, "order", (torch.int32,))
@@ -334,7 +336,8 @@ def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N:
         rp[p] = recv[p].data_ptr()
     rc = lib().arepi_emu_peer_producer(ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p),
                                        _ptr(ready_in), _ptr(order), order.shape[0], M, N, R, owner,
-                                       flag_tile_m, flag_tile_n, scope, workgroups, _stream(stream))
+                                       flag_tile_m, flag_tile_n, scope, workgroups, items_per_release,
+                                       _stream(stream))
     _check(rc, "emu_peer_producer")
 
 

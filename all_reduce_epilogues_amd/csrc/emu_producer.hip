@@ -1,9 +1,12 @@
 // emu_producer.hip -- stands in for the R-1 peer ranks on one GPU (tests and
-// benchmark only).  Each workgroup lands one (peer, flag tile) item: it copies
-// that tile of the peer's partial into recv[peer], drains its stores, meets the
-// workgroup barrier, and one thread publishes the tile's bit with a release --
-// the per-tile readiness of DeepGEMM PR #1 "Fused ring RS: per-tile bitmask",
-// in the place of a per-segment flag.
+// benchmark only).  A workgroup lands a batch of (peer, flag tile) items: it
+// copies those tiles of the peers' partials into recv[peer], drains its
+// stores, meets the workgroup barrier, and one thread publishes the batch's
+// bits after one release -- the per-tile readiness of DeepGEMM PR #1 "Fused
+// ring RS: per-tile bitmask", in the place of a per-segment flag.  A release
+// at agent scope writes back the L2 of the XCD it runs on, which a remote
+// peer's release would not do to this GPU; batching several tiles per release
+// keeps that cost of the emulation down.
 #include <algorithm>
 #include <string>
 
@@ -21,14 +24,20 @@ struct EmuParams {
     const int32_t *order;  // [n_items][2] = (peer, tile)
     int64_t n_items, seg, N, ftiles_n, ftiles, fwords;
     int ftm, ftn, R, owner, system_scope;
+    int per_release;  // items landed per release
 };
 
-// Lands one (peer, flag tile) item with the whole workgroup.
-__device__ void land_item(const EmuParams &p, const int64_t item) {
-    const int peer = p.order[2 * item];
-    const int64_t t = p.order[2 * item + 1];
-    const bool valid = peer >= 0 && peer < p.R && peer != p.owner && t >= 0 && t < p.ftiles;
-    if (!valid) return;  // uniform across the workgroup
+__device__ bool item_valid(const EmuParams &p, const int64_t item, int &peer, int64_t &t) {
+    peer = p.order[2 * item];
+    t = p.order[2 * item + 1];
+    return peer >= 0 && peer < p.R && peer != p.owner && t >= 0 && t < p.ftiles;
+}
+
+// Copies one (peer, flag tile) item with the whole workgroup (no drain).
+__device__ void copy_item(const EmuParams &p, const int64_t item) {
+    int peer;
+    int64_t t;
+    if (!item_valid(p, item, peer, t)) return;  // uniform across the workgroup
     const int64_t r0 = (t / p.ftiles_n) * p.ftm, c0 = (t % p.ftiles_n) * p.ftn;
     const int64_t rows = min((int64_t)p.ftm, p.seg - r0);
     const int64_t packs = min((int64_t)p.ftn, p.N - c0) / 8;
@@ -66,19 +75,30 @@ __device__ void land_item(const EmuParams &p, const int64_t item) {
             if (i < total) store16_nt(d + at(i), v[k]);
         }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const bool sys = p.system_scope != 0;
-        fence_release(sys);
-        fetch_or_relaxed(p.ready_in + (int64_t)peer * p.fwords + (t >> 5), 1u << (t & 31), sys);
-    }
 }
 
-// Workgroup g lands items g, g + G, g + 2G, ... (G = grid size), so a grid
-// smaller than the item count paces the landing like a link of bounded rate.
+// Batch j is items [j*K, j*K + K) in order (K = per_release).  Workgroup g
+// lands batches g, g + G, g + 2G, ... (G = grid size), so a grid smaller than
+// the batch count paces the landing like a link of bounded rate.  Each batch:
+// copies, drain, barrier, one release, then its bits.
 __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
-    for (int64_t item = blockIdx.x; item < p.n_items; item += gridDim.x) land_item(p, item);
+    const int64_t K = p.per_release, batches = (p.n_items + K - 1) / K;
+    for (int64_t j = blockIdx.x; j < batches; j += gridDim.x) {
+        const int64_t i0 = j * K, i1 = min(i0 + K, p.n_items);
+        for (int64_t item = i0; item < i1; ++item) copy_item(p, item);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const bool sys = p.system_scope != 0;
+            fence_release(sys);
+            for (int64_t item = i0; item < i1; ++item) {
+                int peer;
+                int64_t t;
+                if (item_valid(p, item, peer, t))
+                    fetch_or_relaxed(p.ready_in + (int64_t)peer * p.fwords + (t >> 5), 1u << (t & 31), sys);
+            }
+        }
+    }
 }
 
 }  // namespace
@@ -89,7 +109,7 @@ using namespace arepi;
 extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
                                        const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
                                        int owner, int flag_tile_m, int flag_tile_n, int scope,
-                                       int workgroups, arepi_stream_t stream) {
+                                       int workgroups, int items_per_release, arepi_stream_t stream) {
     auto bad = [](const std::string &m) { return fail(AREPI_EINVAL, "arepi_emu_peer_producer: " + m); };
     if (R < 1 || R > kMaxR) return bad("R=" + std::to_string(R) + " outside [1, 8]");
     if (owner < 0 || owner >= R) return bad("owner outside [0, R-1]");
@@ -99,7 +119,8 @@ extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *con
         return bad("flag tile needs flag_tile_m >= 1 and flag_tile_n a positive multiple of 8");
     if (scope != AREPI_SCOPE_AGENT && scope != AREPI_SCOPE_SYSTEM) return bad("scope must be AGENT or SYSTEM");
     if (n_items < 0 || n_items > (int64_t)1 << 30) return bad("n_items out of range");
-    if (workgroups < 0) return bad("workgroups must be >= 0 (0: one per item)");
+    if (workgroups < 0) return bad("workgroups must be >= 0 (0: one per batch)");
+    if (items_per_release < 1) return bad("items_per_release must be >= 1");
     if (n_items == 0) return ok();
     if (!src || !recv || !ready_in || !order) return bad("src, recv, ready_in and order must be non-NULL");
     EmuParams p{};
@@ -123,7 +144,9 @@ extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *con
     p.R = R;
     p.owner = owner;
     p.system_scope = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
-    const int64_t groups = workgroups == 0 ? n_items : std::min<int64_t>(workgroups, n_items);
+    p.per_release = items_per_release;
+    const int64_t batches = (n_items + items_per_release - 1) / items_per_release;
+    const int64_t groups = workgroups == 0 ? batches : std::min<int64_t>(workgroups, batches);
     hipLaunchKernelGGL(emu_producer_kernel, dim3((unsigned)groups), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), p);
     return check_launch("arepi_emu_peer_producer");

@@ -3,15 +3,18 @@
 Prints ONE JSON line.  Headline (`value`): GEMM + reduce-scatter epilogue on
 the tp=4 share -- X [4096,2048] . W [2048,4096] bf16, R=4, owner segment of 1024
 rows, three peer partials landed per 128x128 flag tile by an emulated-peer
-producer on a second stream in shuffled order -- as TFLOP/s of the whole step
-(2*M*N*K per step).  Inputs are resident in HBM before timing starts.
+producer on a second stream in shuffled order, their ready bits published
+eight tiles per release -- as TFLOP/s of the whole step (2*M*N*K per step).
+The same step with one release per tile is reported beside it.  Inputs are
+resident in HBM before timing starts.
 
 Also reported in the same run: the Lamport AR+RMSNorm consumer (8 x
 [4096,7168]) and the weighted top-8 combine ([4096,8,7168]) as GB/s of
 algorithmic bytes, each against the 8 TB/s HBM peak; the pre-staged tp=4
 kernel; the push-ring form of the same GEMM (one hop: the producer landing the
-upstream partials beside it, and pre-staged); with --sweep the tp=8 sweep
-(M = 256..8192, N=7168, K=2048) in both forms.
+upstream partials beside it, and pre-staged); the fp8 block-scaled form
+(pre-staged, against the fp8 peak); the two-phase Lamport call; with --sweep
+the tp=8 sweep (M = 256..8192, N=7168, K=2048) in the bf16 forms.
 
 `cpu_baseline` times the CPU oracle (oracle/, test infrastructure) on a
 bounded row sample of the headline workload.
@@ -34,6 +37,23 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 LAMPORT_BYTES = 998_258_688 + 7168 * 2   # read 8P + write P + re-arm 8P (+ gamma)
 LAMPORT_BYTES_NO_REARM = 528_482_304 + 7168 * 2
 COMBINE_BYTES = 528_613_376              # read x + gate + write out
+# The emulated peers publish their tiles' ready bits eight tiles per release.
+# On one GPU an agent-scope release writes back the L2 of the XCD it runs on --
+# the L2 the GEMM is using -- which a remote peer's release never does to this
+# GPU; one release per tile costs the step ~17 us of that artifact.  The step
+# with one release per tile is reported beside the headline.
+PRODUCER_TILES_PER_RELEASE = 8
+
+_side_stream = None
+
+
+def side_stream(torch):
+    """One second stream for every leg: streams share a few hardware queues,
+    and a fresh stream per leg can land on the main stream's queue."""
+    global _side_stream
+    if _side_stream is None:
+        _side_stream = torch.cuda.Stream()
+    return _side_stream
 # two-phase Lamport, one rank's call at [4096,7168]: phase A reads P and stores
 # P (its part into 8 stagings), phase B reads P, re-arms P, writes out P (+gamma)
 LAMPORT2_BYTES = 5 * 58_720_256 + 7168 * 2
@@ -98,7 +118,7 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs=0):
+def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs=0, per_release=1):
     """tp=4 share; a producer stream lands the peers while the GEMM runs
     (ring=True: the push-ring hop, the producer landing the upstream partials).
 
@@ -140,7 +160,7 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
     send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
+    side = side_stream(torch)
     tile = A.gemm_rs_pick_tile(M, N, K, R, owner, publish=True)
     n_ev = steps + warmup
     H = _HipEvents()
@@ -151,7 +171,7 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
         if i > 0:
             H.wait(side, ev_ge[i - 1])
         A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, absent, M, N, workgroups=producer_wgs,
-                            stream=side)
+                            items_per_release=per_release, stream=side)
         H.record(ev_gs[i], main)
         if ring:
             A.gemm_rs_ring(x, w, recv, rin, out, send, R, owner, ready_out=rout,
@@ -249,7 +269,7 @@ def lamport(A, inputs, torch, steps, warmup):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     A.lamport_prefill(st)   # arming: once, before any timing
     main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
+    side = side_stream(torch)
     n = steps + warmup
     # fence-free HIP events on the consumer's stream, as for the GEMM
     H = _HipEvents()
@@ -333,7 +353,7 @@ def lamport_2phase(A, inputs, torch, steps, warmup):
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     main = torch.cuda.current_stream()
-    side = torch.cuda.Stream()
+    side = side_stream(torch)
     n = steps + warmup
     # fence-free HIP events on the consumer's stream, as for the GEMM
     H = _HipEvents()
@@ -449,7 +469,11 @@ def main():
     secondary = {}
     head = None
     if a.only in (None, "gemm_rs"):
-        head = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup)
+        head = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, per_release=PRODUCER_TILES_PER_RELEASE)
+        r1 = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, per_release=1)
+        secondary["gemm_rs_tp4_step_one_release_per_tile"] = dict(
+            ms_per_step=r1["ms_per_step"], tflops=r1["tflops"], kernel_ms=r1["gemm_ms"],
+            frac_mfma=r1["gemm_tflops"] / PEAK_BF16_TFLOPS)
     if a.only in (None, "lamport"):
         secondary["lamport_ar_rmsnorm"] = lamport(A, inputs, torch, max(10, a.steps // 2), 3)
     if a.only in (None, "combine"):
@@ -459,7 +483,7 @@ def main():
     if a.only in (None, "gemm_rs", "gemm_rs_prestaged"):
         secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2)
     if a.only in (None, "gemm_rs_ring"):
-        r = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, ring=True)
+        r = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, ring=True, per_release=PRODUCER_TILES_PER_RELEASE)
         secondary["gemm_rs_ring_tp4_step"] = dict(ms_per_step=r["ms_per_step"], tflops=r["tflops"],
                                                   kernel_ms=r["gemm_ms"], kernel_tflops=r["gemm_tflops"],
                                                   frac_mfma=r["gemm_tflops"] / PEAK_BF16_TFLOPS, tile=r["tile"])
@@ -488,8 +512,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": "gemm_rs tp4 share: X[4096,2048] x W[2048,4096] bf16, R=4, owner=0, "
                                "3 peer partials [1024,4096] landed per 128x128 flag tile by a producer "
-                               "stream in shuffled order; send + ready_out published",
+                               "stream in shuffled order, their bits published 8 tiles per release; "
+                               "send + ready_out published",
                    "M": 4096, "N": 4096, "K": 2048, "R": 4, "owner": 0,
+                   "producer_tiles_per_release": PRODUCER_TILES_PER_RELEASE,
                    "tile": head["tile"] if head else None},
     }
     if head:

@@ -306,15 +306,19 @@ int arepi_combine_reduce_lds(const uint16_t *x, const float *gate, uint16_t *out
  * t): copy flag tile t of src[p] (bf16 [M/R,N]) into recv[p], then set bit t
  * of ready_in[p] with a release at `scope`.  src and recv are HOST arrays of R
  * device pointers (entry `owner` ignored); ready_in must be zero beforehand.
- * workgroups = 0 lands every item at once (one workgroup each); workgroups =
- * G > 0 lands them G at a time, in order, which paces the arrivals like a link
- * of bounded rate and leaves the other compute units to the consumer.
- * Errors: EINVAL for bad shapes, NULL pointers or workgroups < 0.
+ * Items go in batches of items_per_release consecutive entries of order: a
+ * batch's tiles are copied, then one release at `scope` precedes the batch's
+ * bits (1 = a release per tile).  workgroups = 0 lands every batch at once
+ * (one workgroup each); workgroups = G > 0 lands them G at a time, in order,
+ * which paces the arrivals like a link of bounded rate and leaves the other
+ * compute units to the consumer.
+ * Errors: EINVAL for bad shapes, NULL pointers, workgroups < 0 or
+ * items_per_release < 1.
  * ------------------------------------------------------------------------ */
 int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
                             const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
                             int owner, int flag_tile_m, int flag_tile_n, int scope, int workgroups,
-                            arepi_stream_t stream);
+                            int items_per_release, arepi_stream_t stream);
 
 /* Test-only: phase A of the two-phase Lamport call for rank `rank` alone
  * (stands in for a peer GPU's phase A on one GPU).  Same arguments and
