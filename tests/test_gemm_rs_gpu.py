@@ -185,7 +185,7 @@ def test_tp4_workload_prestaged_and_concurrent_producer():
     # partials in a shuffled tile order while the GEMM runs
     dev = device()
     tiles = oracle.flag_tiles(M, N, R, 128, 128)
-    for seed, groups in ((11, 0), (12, 0), (13, 24)):
+    for seed, groups, per_release in ((11, 0, 1), (12, 0, 1), (13, 24, 1), (14, 0, 8), (15, 16, 4)):
         order = torch.from_numpy(inputs.producer_order(R, owner, tiles, seed)).to(dev)
         src = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
         recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
@@ -198,7 +198,8 @@ def test_tp4_workload_prestaged_and_concurrent_producer():
         torch.cuda.synchronize()
         side = torch.cuda.Stream()
         main = torch.cuda.current_stream()
-        A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, workgroups=groups, stream=side)
+        A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, workgroups=groups,
+                            items_per_release=per_release, stream=side)
         A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, status=status, stream=main)
         torch.cuda.synchronize()
         assert int(status.item()) == 0, "a readiness wait timed out"
