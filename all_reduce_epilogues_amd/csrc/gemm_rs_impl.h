@@ -623,26 +623,35 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
             if (more) gload(b + 1);
             const lds_t *As = S0 + (b & 1) * ST8;
             const lds_t *Bs = As + A8;
+            // Pairs of 16-wide MFMA steps from one 16-byte read per lane: lane
+            // half h reads chunk 2m+h of its row (k = 32m + 16h .. +15); its
+            // low 8 bytes feed step 2m and its high 8 bytes step 2m+1.  A and
+            // B use the same k assignment, so each pair still sums the
+            // products of all 32 k of its chunks.
 #pragma unroll
-            for (int s8 = 0; s8 < 8; ++s8) {
-                long av[TM], bv[TN];
+            for (int m2 = 0; m2 < 4; ++m2) {
+                i32x4 aq[TM], bq[TN];
+                const int c = 2 * m2 + (lane >> 5);
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     const int v = wm * WM + i * 32 + (lane & 31);
-                    av[i] = *(const __attribute__((address_space(3))) long *)(As + v * ROWB + ((s8 ^ swz8(v)) << 4) +
-                                                                             8 * (lane >> 5));
+                    aq[i] = *(const __attribute__((address_space(3))) i32x4 *)(As + v * ROWB + ((c ^ swz8(v)) << 4));
                 }
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     const int v = wn * WN + j * 32 + (lane & 31);
-                    bv[j] = *(const __attribute__((address_space(3))) long *)(Bs + v * ROWB + ((s8 ^ swz8(v)) << 4) +
-                                                                             8 * (lane >> 5));
+                    bq[j] = *(const __attribute__((address_space(3))) i32x4 *)(Bs + v * ROWB + ((c ^ swz8(v)) << 4));
                 }
 #pragma unroll
-                for (int i = 0; i < TM; ++i)
+                for (int half = 0; half < 2; ++half)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av[i], bv[j], acc[i][j], 0, 0, 0);
+                    for (int i = 0; i < TM; ++i)
+#pragma unroll
+                        for (int j = 0; j < TN; ++j) {
+                            const long a8 = (long)(uint32_t)aq[i][2 * half] | ((long)(uint32_t)aq[i][2 * half + 1] << 32);
+                            const long b8 = (long)(uint32_t)bq[j][2 * half] | ((long)(uint32_t)bq[j][2 * half + 1] << 32);
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a8, b8, acc[i][j], 0, 0, 0);
+                        }
             }
             // after block b: acc *= s_b / s_{b+1} (s_last after the last block);
             // the factors were written before the barrier that ended step b-1
