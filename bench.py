@@ -474,6 +474,11 @@ def main():
         secondary["gemm_rs_tp4_step_one_release_per_tile"] = dict(
             ms_per_step=r1["ms_per_step"], tflops=r1["tflops"], kernel_ms=r1["gemm_ms"],
             frac_mfma=r1["gemm_tflops"] / PEAK_BF16_TFLOPS)
+    if a.only in (None, "gemm_rs_ring"):
+        r = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, ring=True, per_release=PRODUCER_TILES_PER_RELEASE)
+        secondary["gemm_rs_ring_tp4_step"] = dict(ms_per_step=r["ms_per_step"], tflops=r["tflops"],
+                                                  kernel_ms=r["gemm_ms"], kernel_tflops=r["gemm_tflops"],
+                                                  frac_mfma=r["gemm_tflops"] / PEAK_BF16_TFLOPS, tile=r["tile"])
     if a.only in (None, "lamport"):
         secondary["lamport_ar_rmsnorm"] = lamport(A, inputs, torch, max(10, a.steps // 2), 3)
     if a.only in (None, "combine"):
@@ -482,11 +487,6 @@ def main():
         secondary["lamport_2phase_ar_rmsnorm"] = lamport_2phase(A, inputs, torch, max(10, a.steps // 2), 3)
     if a.only in (None, "gemm_rs", "gemm_rs_prestaged"):
         secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2)
-    if a.only in (None, "gemm_rs_ring"):
-        r = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, ring=True, per_release=PRODUCER_TILES_PER_RELEASE)
-        secondary["gemm_rs_ring_tp4_step"] = dict(ms_per_step=r["ms_per_step"], tflops=r["tflops"],
-                                                  kernel_ms=r["gemm_ms"], kernel_tflops=r["gemm_tflops"],
-                                                  frac_mfma=r["gemm_tflops"] / PEAK_BF16_TFLOPS, tile=r["tile"])
     if a.only in (None, "gemm_rs_fp8"):
         secondary["gemm_rs_fp8_tp4_prestaged"] = gemm_rs_fp8_prestaged(A, inputs, torch, a.steps, a.warmup)
     if a.only in (None, "gemm_rs_ring", "gemm_rs_ring_prestaged"):
