@@ -155,6 +155,7 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
         case AREPI_TILE_128x256_S3: launch<128, 256, 64, 128, 32, 3, 2>(p, s); break;
         case AREPI_TILE_128x128_S4: launch<128, 128, 64, 64, 32, 4, 2>(p, s); break;
         case AREPI_TILE_256x256_W8: launch<256, 256, 128, 64, 32, 4, 2>(p, s); break;
+        case AREPI_TILE_256x256_W8_K64: launch<256, 256, 128, 64, 64, 2, 2>(p, s); break;
         default: return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_fused: no kernel for tile " + std::to_string(cfg));
     }
     return check_launch("arepi_gemm_rs_fused");

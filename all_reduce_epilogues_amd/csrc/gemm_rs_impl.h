@@ -1028,6 +1028,7 @@ struct TileCfg {
 // eff: sustained per-CU throughput relative to the 4-stage 256x256 tile, from
 // timing the tp=4 / tp=8 workloads on MI355X (contiguous rows).
 constexpr TileCfg kTiles[] = {
+    {AREPI_TILE_256x256_W8_K64, 256, 256, 1, 1.14},
     {AREPI_TILE_256x256_W8, 256, 256, 1, 1.08},
     {AREPI_TILE_256x256_S4, 256, 256, 1, 1.00},
     {AREPI_TILE_256x256, 256, 256, 1, 0.96},

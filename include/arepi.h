@@ -71,6 +71,7 @@ enum {
     AREPI_TILE_128x256_S3 = 8,
     AREPI_TILE_128x128_S4 = 9,
     AREPI_TILE_256x256_W8 = 10, /* 8 waves (two per SIMD), BK 32, 4 stages */
+    AREPI_TILE_256x256_W8_K64 = 11, /* 8 waves, BK 64, 2 stages: half the barriers per K */
     /* ORed into an explicit tile: when every segment is a whole number of
      * half-blocks (BM/2 rows, BM >= 64), a workgroup takes two half-blocks and
      * the owner segment's half-blocks are each paired with a non-owner one,
