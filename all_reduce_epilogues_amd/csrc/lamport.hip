@@ -481,14 +481,14 @@ extern "C" int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma
 #define AREPI_RMS_LAUNCH(P, T)                                                                                   \
     hipLaunchKernelGGL((ar_rmsnorm_kernel<P, T>), dim3((unsigned)M), dim3(T), 0, s, staging, gamma, out, M, N, S, \
                        eps, sys, status, lim)
+    // 512-thread rows from 257 packs up: at N = 7168 (896 packs, two per
+    // thread) this timed ~1% faster than 256 threads with four packs each
     if (ppt <= 1)
         AREPI_RMS_LAUNCH(1, 256);
-    else if (ppt <= 2)
-        AREPI_RMS_LAUNCH(2, 256);
-    else if (ppt <= 4)
-        AREPI_RMS_LAUNCH(4, 256);
+    else if (packs <= 1024)
+        AREPI_RMS_LAUNCH(2, 512);
     else
-        AREPI_RMS_LAUNCH(8, 256);
+        AREPI_RMS_LAUNCH(4, 512);
 #undef AREPI_RMS_LAUNCH
     return check_launch("arepi_ar_rmsnorm_lamport");
 }
