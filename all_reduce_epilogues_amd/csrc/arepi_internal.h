@@ -52,6 +52,7 @@ __device__ __forceinline__ void store16_nt(void *p, uint4 v) {
 // gfx9 buffer-resource word 3 (raw, untyped 32-bit data format).
 constexpr int kBufferDword3 = 0x00020000;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Cache-policy operand of the direct-to-LDS load builtins for a streaming
 // (nt) load on gfx950 (checked against the emitted assembly).

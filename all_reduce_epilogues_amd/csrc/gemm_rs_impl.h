@@ -520,7 +520,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         // [N,K] (both K-contiguous bytes); one 128-wide K block per step
         // through two LDS stages of [BM][128] + [BN][128] bytes whose 16-byte
         // chunks are XOR-swizzled by row.  Each block's product d_b is
-        // accumulated on v_mfma_f32_32x32x16_fp8_fp8 into the one accumulator
+        // accumulated on the 64-wide fp8 MFMA into the one accumulator
         // set, which carries the running sum rescaled: after block b,
         // acc *= s_b / s_{b+1} (s_b = xs[m,b] * ws[n/128,b]), and after the
         // last block acc *= s_last, so acc ends at sum_b s_b * d_b.  The tile's
@@ -623,35 +623,38 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
             if (more) gload(b + 1);
             const lds_t *As = S0 + (b & 1) * ST8;
             const lds_t *Bs = As + A8;
-            // Pairs of 16-wide MFMA steps from one 16-byte read per lane: lane
-            // half h reads chunk 2m+h of its row (k = 32m + 16h .. +15); its
-            // low 8 bytes feed step 2m and its high 8 bytes step 2m+1.  A and
-            // B use the same k assignment, so each pair still sums the
-            // products of all 32 k of its chunks.
+            // Two 64-wide MFMA steps per block (v_mfma_scale_f32_32x32x64_f8f6f4
+            // with unit scales: the full fp8 rate on gfx950, where the 16-wide
+            // fp8 MFMA runs at the bf16 rate).  Lane half h of step s takes
+            // chunks 4s+h and 4s+2+h of its row (read as 16 bytes each) as its
+            // 32 operand bytes.  A and B use the same k assignment, so each
+            // step sums the products of all 64 k of its four chunks.
 #pragma unroll
-            for (int m2 = 0; m2 < 4; ++m2) {
-                i32x4 aq[TM], bq[TN];
-                const int c = 2 * m2 + (lane >> 5);
+            for (int s = 0; s < 2; ++s) {
+                i32x4 aq[2][TM], bq[2][TN];
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int v = wm * WM + i * 32 + (lane & 31);
-                    aq[i] = *(const __attribute__((address_space(3))) i32x4 *)(As + v * ROWB + ((c ^ swz8(v)) << 4));
+                for (int q = 0; q < 2; ++q) {
+                    const int c = 4 * s + 2 * q + (lane >> 5);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) {
+                        const int v = wm * WM + i * 32 + (lane & 31);
+                        aq[q][i] = *(const __attribute__((address_space(3))) i32x4 *)(As + v * ROWB + ((c ^ swz8(v)) << 4));
+                    }
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) {
+                        const int v = wn * WN + j * 32 + (lane & 31);
+                        bq[q][j] = *(const __attribute__((address_space(3))) i32x4 *)(Bs + v * ROWB + ((c ^ swz8(v)) << 4));
+                    }
                 }
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int v = wn * WN + j * 32 + (lane & 31);
-                    bq[j] = *(const __attribute__((address_space(3))) i32x4 *)(Bs + v * ROWB + ((c ^ swz8(v)) << 4));
-                }
+                for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int half = 0; half < 2; ++half)
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j) {
-                            const long a8 = (long)(uint32_t)aq[i][2 * half] | ((long)(uint32_t)aq[i][2 * half + 1] << 32);
-                            const long b8 = (long)(uint32_t)bq[j][2 * half] | ((long)(uint32_t)bq[j][2 * half + 1] << 32);
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a8, b8, acc[i][j], 0, 0, 0);
-                        }
+                    for (int j = 0; j < TN; ++j) {
+                        const i32x8 a = __builtin_shufflevector(aq[0][i], aq[1][i], 0, 1, 2, 3, 4, 5, 6, 7);
+                        const i32x8 b = __builtin_shufflevector(bq[0][j], bq[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
+                        // formats 0/0: e4m3fn operands; scales 127: 2^0 in E8M0
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 127, 0, 127);
+                    }
             }
             // after block b: acc *= s_b / s_{b+1} (s_last after the last block);
             // the factors were written before the barrier that ended step b-1
