@@ -18,8 +18,8 @@ namespace {
 
 template <int PEERS>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_rs_fp8_kernel(const GemmRsParams p) {
-    // the stages, then 2 x 128 per-row scale factors of the fp8 mainloop
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<256, 128, 64, 2>() + 2 * 256 * 4];
+    // three stages, their 2 KiB scale areas, then 2 x 256 per-row factors
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<256, 128, 64, 3>() + 3 * 2048 + 2 * 256 * 4];
     constexpr int BM = 256, CK = 128;
     int rb, cb;
     tile_of_block(p, blockIdx.x, rb, cb);
@@ -30,9 +30,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool own_a = alen > 0 && a0 < oseg1 && a0 + alen > oseg0;
     const bool own_b = blen > 0 && b0 < oseg1 && b0 + blen > oseg0;
     if (!own_a && !own_b)
-        gemm_rs_body<256, 128, 64, 64, 64, 2, 2, PEERS, kNoOwnerRows, true>(p, smem, rb, cb, a0, alen, b0, blen);
+        gemm_rs_body<256, 128, 64, 64, 64, 3, 2, PEERS, kNoOwnerRows, true>(p, smem, rb, cb, a0, alen, b0, blen);
     else
-        gemm_rs_body<256, 128, 64, 64, 64, 2, 2, PEERS, kOwnerRowsAnywhere, true>(p, smem, rb, cb, a0, alen, b0,
+        gemm_rs_body<256, 128, 64, 64, 64, 3, 2, PEERS, kOwnerRowsAnywhere, true>(p, smem, rb, cb, a0, alen, b0,
                                                                                  blen);
 }
 

@@ -518,88 +518,115 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     } else {
         // ---- fp8 e4m3fn block-scaled mainloop.  X [M,K] and W transposed
         // [N,K] (both K-contiguous bytes); one 128-wide K block per step
-        // through two LDS stages of [BM][128] + [BN][128] bytes whose 16-byte
-        // chunks are XOR-swizzled by row.  Each block's product d_b is
-        // accumulated on the 64-wide fp8 MFMA into the one accumulator
-        // set, which carries the running sum rescaled: after block b,
-        // acc *= s_b / s_{b+1} (s_b = xs[m,b] * ws[n/128,b]), and after the
-        // last block acc *= s_last, so acc ends at sum_b s_b * d_b.  The tile's
-        // columns lie in one 128-column scale block (BN == 128, n0 a multiple
-        // of 128).  The kernel allocates 2*BM floats of LDS past the stages
-        // for the per-row factors.
+        // through an S-stage LDS ring of [BM][128] + [BN][128] bytes whose
+        // 16-byte chunks are XOR-swizzled by row, filled by direct-to-LDS
+        // loads as in the bf16 ring.  Each block's product d_b is accumulated
+        // on the 64-wide fp8 MFMA into the one accumulator set, which carries
+        // the running sum rescaled: after block b, acc *= s_b / s_{b+1}
+        // (s_b = xs[m,b] * ws[n/128,b]), and after the last block acc *=
+        // s_last, so acc ends at sum_b s_b * d_b.  The tile's columns lie in
+        // one 128-column scale block (BN == 128, n0 a multiple of 128).  The
+        // kernel allocates, past the stages, S scale areas of 2 KiB and 2*BM
+        // floats of per-row factors.
         static_assert(BN == 128, "one W scale block per tile");
         // Chunk c of tile row v sits at c ^ swz8(v).  Two 128-byte rows share a
         // 256-byte line of the 64 banks; ((v >> 1) & 7) sends the 16 rows of
-        // one parity to 8 positions twice each, so the 8-byte operand reads of
-        // 32 consecutive rows take the minimum two passes.
+        // one parity to 8 positions twice each, so the 16-byte operand reads of
+        // 32 consecutive rows take the minimum passes.
         auto swz8 = [](int v) { return (v >> 1) & 7; };
         constexpr int ROWB = 128;  // bytes of one tile row per step
         constexpr int A8 = BM * ROWB, B8 = BN * ROWB, ST8 = A8 + B8;
-        static_assert(2 * ST8 <= LDS_BYTES, "two fp8 stages fit the stage memory");
-        constexpr int NTH = NW * 64;
-        constexpr int ACH = A8 / 16 / NTH, BCH = B8 / 16 / NTH;  // 16-byte chunks per thread per step
-        static_assert(ACH * NTH * 16 == A8 && BCH * NTH * 16 == B8, "fp8 tile split");
+        static_assert(S * ST8 == LDS_BYTES, "the fp8 stages fill the stage memory");
+        constexpr int AI = A8 / (NW * 1024), BI = B8 / (NW * 1024);  // 1 KiB load instructions per wave per step
+        static_assert(AI * NW * 1024 == A8 && BI * NW * 1024 == B8, "fp8 tile split");
+        static_assert(BM == 4 * 64 && NW >= 5, "scale loads: four waves of row scales and one column scale");
+        constexpr int ND8 = AI + BI + 1;  // loads per wave per step (operands, then one of scales)
+        static_assert(S >= 2 && (S - 2) * ND8 < 64, "stage count vs vmcnt range");
+        constexpr int SCL = 2048;  // bytes of one stage's scale area: 8 waves x 64 lanes x 4
         const int KB = (int)(K / 128);
         const int nb = (int)(n0 / 128);
-        // byte offsets are 32-bit: M*K, N*K < 2^30 (host-checked)
-        const __amdgpu_buffer_rsrc_t x8r = __builtin_amdgcn_make_buffer_rsrc((void *)p.x, 0, (int)(M * K), kBufferDword3);
-        const __amdgpu_buffer_rsrc_t w8r = __builtin_amdgcn_make_buffer_rsrc((void *)p.w, 0, (int)(N * K), kBufferDword3);
-        uint32_t a_src[ACH], b_src[BCH];
-        int a_dst[ACH], b_dst[BCH];
+        // byte offsets are 32-bit: M*K, N*K < 2^30 and M*KB*4 < 2^31 (host-checked)
+        const i32x4 x8r = buffer_rsrc(p.x, (uint32_t)(M * K));
+        const i32x4 w8r = buffer_rsrc(p.w, (uint32_t)(N * K));
+        const i32x4 xsr = buffer_rsrc(p.xs, (uint32_t)(M * KB * 4));
+        const i32x4 wsr = buffer_rsrc(p.ws, (uint32_t)(((N + 127) / 128) * KB * 4));
+        // Per-lane sources.  Instruction i of a wave fills 1 KiB: 8 tile rows
+        // of 8 chunks; the lane writes physical chunk lane%8 of its row and
+        // loads the logical chunk the read side expects there.
+        uint32_t xo[AI], wo[BI];
 #pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int c = tid + i * NTH, v = c / 8, k16 = c % 8;
+        for (int i = 0; i < AI; ++i) {
+            const int v = (wave * AI + i) * 8 + lane / 8;
             const int64_t gm = row_of(v);
-            a_src[i] = gm >= 0 ? (uint32_t)(gm * K + k16 * 16) : kOob;
-            a_dst[i] = v * ROWB + ((k16 ^ swz8(v)) << 4);
+            xo[i] = gm >= 0 ? (uint32_t)(gm * K + (((lane & 7) ^ swz8(v)) << 4)) : kOob;
         }
 #pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int c = tid + i * NTH, v = c / 8, k16 = c % 8;
+        for (int i = 0; i < BI; ++i) {
+            const int v = (wave * BI + i) * 8 + lane / 8;
             const int64_t gn = n0 + v;
-            b_src[i] = gn < N ? (uint32_t)(gn * K + k16 * 16) : kOob;
-            b_dst[i] = A8 + v * ROWB + ((k16 ^ swz8(v)) << 4);
+            wo[i] = gn < N ? (uint32_t)(gn * K + (((lane & 7) ^ swz8(v)) << 4)) : kOob;
         }
-        i32x4 ra[ACH], rb[BCH];
-        auto gload = [&](int b) {
-            const uint32_t kb = (uint32_t)b * 128u;
-#pragma unroll
-            for (int i = 0; i < ACH; ++i)
-                ra[i] = __builtin_bit_cast(
-                    i32x4, __builtin_amdgcn_raw_buffer_load_b128(x8r, a_src[i] == kOob ? kOob : a_src[i] + kb, 0, 0));
-#pragma unroll
-            for (int i = 0; i < BCH; ++i)
-                rb[i] = __builtin_bit_cast(
-                    i32x4, __builtin_amdgcn_raw_buffer_load_b128(w8r, b_src[i] == kOob ? kOob : b_src[i] + kb, 0, 0));
+        // Scales ride one block ahead: the loads of step kt bring block kt+1's
+        // scales into stage kt's scale area -- waves 0..3 the row scales of
+        // tile rows 64*wave + lane (slot = tile row), wave 4 lane 0 the
+        // column scale (slot 256); every other lane reads nothing (zeros).
+        const i32x4 sr = wave_u < 4 ? xsr : wsr;
+        uint32_t so;
+        {
+            const int64_t gm = wave < 4 ? row_of(wave * 64 + lane) : -1;
+            so = wave < 4 ? (gm >= 0 ? (uint32_t)(gm * KB * 4) : kOob)
+                          : (wave == 4 && lane == 0 ? (uint32_t)((int64_t)nb * KB * 4) : kOob);
+        }
+        lds_t *const SC = S0 + LDS_BYTES;                                   // [S][SCL]
+        float *const fac = reinterpret_cast<float *>(smem + LDS_BYTES + S * SCL);  // [2][BM]
+        auto dma4 = [](i32x4 rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                         :
+                         : "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff)
+                         : "memory", "m0");
         };
-        auto lstore = [&](int stage) {
-            lds_t *base = S0 + stage * ST8;
+        // Loads of step kt into stage kt % S: exactly ND8 per wave for every kt
+        // (past the last block every offset is out of range and loads zeros),
+        // so the vmcnt arithmetic is uniform.
+        auto issue8 = [&](int kt) {
+            const lds_t *st = S0 + (kt % S) * ST8;
+            const uint32_t la = lds_addr(st) + wave_u * AI * 1024;
+            const uint32_t lb = lds_addr(st + A8) + wave_u * BI * 1024;
+            const bool in = kt < KB;
+            // (kt is uniform; readfirstlane tells the compiler so for the scalar operands)
+            const uint32_t k0 = __builtin_amdgcn_readfirstlane(in ? (uint32_t)kt * 128u : 0u);
+            const uint32_t la_u = __builtin_amdgcn_readfirstlane(la), lb_u = __builtin_amdgcn_readfirstlane(lb);
 #pragma unroll
-            for (int i = 0; i < ACH; ++i) *(__attribute__((address_space(3))) i32x4 *)(base + a_dst[i]) = ra[i];
+            for (int i = 0; i < AI; ++i) dma16(x8r, la_u + i * 1024, in ? xo[i] : kOob, k0);
 #pragma unroll
-            for (int i = 0; i < BCH; ++i) *(__attribute__((address_space(3))) i32x4 *)(base + b_dst[i]) = rb[i];
+            for (int i = 0; i < BI; ++i) dma16(w8r, lb_u + i * 1024, in ? wo[i] : kOob, k0);
+            const bool sin = kt + 1 < KB;
+            dma4(sr, __builtin_amdgcn_readfirstlane(lds_addr(SC + (kt % S) * SCL) + wave_u * 256), sin ? so : kOob,
+                 __builtin_amdgcn_readfirstlane(sin ? (uint32_t)(kt + 1) * 4u : 0u));
         };
-        // Per-row factors through LDS (past the stages; the kernel allocates
-        // them): before step b's barrier, threads t < BM write for tile row t
-        // the factor applied after block b, s_b/s_{b+1} (or s_last after the
-        // last block), into buffer b&1; after the barrier every lane reads the
-        // factors of its own accumulator rows.  One division per row and block
-        // instead of one per lane.  Rows past the end get factor 1 (their
-        // products are zero).
-        float *const fac = reinterpret_cast<float *>(smem + LDS_BYTES);  // [2][BM]
+        // Factors: thread t < BM keeps its row's current scale s_b and column
+        // scale in registers; at the top of step b it reads block b+1's from
+        // the scale area of stage b%S (landed with step b's operands) and
+        // writes the factor applied after block b, s_b/s_{b+1} (or s_last
+        // after the last block), into fac buffer b&1; the barrier that ends the
+        // step publishes it.  One division per row and block.  Rows past the
+        // end get factor 1 (their products are zero).
         const int64_t frow = tid < BM ? row_of(tid) : -1;
-        auto row_scale = [&](int b) -> float {
-            return frow >= 0 ? p.xs[frow * KB + b] : 1.0f;
-        };
-        auto col_scale = [&](int b) -> float { return p.ws[(int64_t)nb * KB + b]; };
-        // factor of this thread's row after block b
+        float rs = frow >= 0 ? p.xs[frow * KB] : 1.0f;
+        float cs = p.ws[(int64_t)nb * KB];
+        asm volatile("" ::"v"(rs), "v"(cs));  // both loads land before the first direct-to-LDS load is issued
         auto write_factor = [&](int b) {
             if (tid < BM) {
                 float f;
-                if (b + 1 < KB)
-                    f = (row_scale(b) / row_scale(b + 1)) * (col_scale(b) / col_scale(b + 1));
-                else
-                    f = row_scale(b) * col_scale(b);
+                if (b + 1 < KB) {
+                    const float *sc = reinterpret_cast<const float *>(smem + LDS_BYTES + (b % S) * SCL);
+                    const float rn = frow >= 0 ? sc[tid] : 1.0f, cn = sc[256];
+                    f = (rs / rn) * (cs / cn);
+                    rs = rn;
+                    cs = cn;
+                } else {
+                    f = rs * cs;
+                }
                 fac[(b & 1) * BM + tid] = f;
             }
         };
@@ -614,14 +641,15 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                     for (int j = 0; j < TN; ++j) acc[i][j][r] *= f;
                 }
         };
-        gload(0);
-        lstore(0);
-        write_factor(0);
+#pragma unroll
+        for (int s0 = 0; s0 < S - 1; ++s0) issue8(s0);
+        wait_vmcnt<(S - 2) * ND8>();
         __syncthreads();
         for (int b = 0; b < KB; ++b) {
-            const bool more = b + 1 < KB;
-            if (more) gload(b + 1);
-            const lds_t *As = S0 + (b & 1) * ST8;
+            // stage b%S holds block b's operands and block b+1's scales
+            write_factor(b);
+            issue8(b + S - 1);  // into stage (b-1)%S, free since the barrier that ended step b-1
+            const lds_t *As = S0 + (b % S) * ST8;
             const lds_t *Bs = As + A8;
             // Two 64-wide MFMA steps per block (v_mfma_scale_f32_32x32x64_f8f6f4
             // with unit scales: the full fp8 rate on gfx950, where the 16-wide
@@ -651,19 +679,16 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
 #pragma unroll
                     for (int j = 0; j < TN; ++j) {
                         const i32x8 a = __builtin_shufflevector(aq[0][i], aq[1][i], 0, 1, 2, 3, 4, 5, 6, 7);
-                        const i32x8 b = __builtin_shufflevector(bq[0][j], bq[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
+                        const i32x8 b8 = __builtin_shufflevector(bq[0][j], bq[1][j], 0, 1, 2, 3, 4, 5, 6, 7);
                         // formats 0/0: e4m3fn operands; scales 127: 2^0 in E8M0
-                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[i][j], 0, 0, 0, 127, 0, 127);
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b8, acc[i][j], 0, 0, 0, 127, 0, 127);
                     }
             }
-            // after block b: acc *= s_b / s_{b+1} (s_last after the last block);
-            // the factors were written before the barrier that ended step b-1
-            apply_factor(b);
-            if (more) {
-                lstore((b + 1) & 1);  // free since the barrier that ended step b-1
-                write_factor(b + 1);  // buffer (b+1)&1: last read in step b-1
-            }
+            // step b+1's loads are done once at most the younger ones are in flight
+            wait_vmcnt<(S - 2) * ND8>();
             __syncthreads();
+            // after block b: acc *= s_b / s_{b+1} (s_last after the last block)
+            apply_factor(b);
         }
     }
     wait_vmcnt_zero();
