@@ -18,8 +18,8 @@ namespace {
 
 template <int PEERS>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_rs_fp8_kernel(const GemmRsParams p) {
-    // three stages, their 2 KiB scale areas, then 2 x 256 per-row factors
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<256, 128, 64, 3>() + 3 * 2048 + 2 * 256 * 4];
+    // two stages, their 2 KiB scale areas, then 2 x 2 x 256 factors
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<256, 256, 64, 2>() + 2 * 2048 + 2 * 2 * 256 * 4];
     constexpr int BM = 256, CK = 128;
     int rb, cb;
     tile_of_block(p, blockIdx.x, rb, cb);
@@ -30,9 +30,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const bool own_a = alen > 0 && a0 < oseg1 && a0 + alen > oseg0;
     const bool own_b = blen > 0 && b0 < oseg1 && b0 + blen > oseg0;
     if (!own_a && !own_b)
-        gemm_rs_body<256, 128, 64, 64, 64, 3, 2, PEERS, kNoOwnerRows, true>(p, smem, rb, cb, a0, alen, b0, blen);
+        gemm_rs_body<256, 256, 128, 64, 64, 2, 2, PEERS, kNoOwnerRows, true>(p, smem, rb, cb, a0, alen, b0, blen);
     else
-        gemm_rs_body<256, 128, 64, 64, 64, 3, 2, PEERS, kOwnerRowsAnywhere, true>(p, smem, rb, cb, a0, alen, b0,
+        gemm_rs_body<256, 256, 128, 64, 64, 2, 2, PEERS, kOwnerRowsAnywhere, true>(p, smem, rb, cb, a0, alen, b0,
                                                                                  blen);
 }
 
@@ -48,11 +48,11 @@ extern "C" int arepi_gemm_rs_fp8_supports(int64_t M, int64_t N, int64_t K, int R
     if (K % 128) return fail(AREPI_EINVAL, "arepi_gemm_rs_fp8: K=" + std::to_string(K) + " must be a multiple of 128");
     if (tile_cfg & ~AREPI_TILE_CONSUME_READY)
         return fail(AREPI_EUNSUPPORTED,
-                    "arepi_gemm_rs_fp8: tile_cfg may only carry AREPI_TILE_CONSUME_READY (the tile is 256x128)");
+                    "arepi_gemm_rs_fp8: tile_cfg may only carry AREPI_TILE_CONSUME_READY (the tile is 256x256)");
     const bool nest = publish || (tile_cfg & AREPI_TILE_CONSUME_READY);
-    if (nest && !flags_nest(M, N, R, flag_tile_m, flag_tile_n, 256, 128))
+    if (nest && !flags_nest(M, N, R, flag_tile_m, flag_tile_n, 256, 256))
         return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_fp8: flag tiles " + std::to_string(flag_tile_m) + "x" +
-                                            std::to_string(flag_tile_n) + " straddle 256x128 compute tiles");
+                                            std::to_string(flag_tile_n) + " straddle 256x256 compute tiles");
     return ok();
 }
 
@@ -99,7 +99,7 @@ extern "C" int arepi_gemm_rs_fp8(const uint8_t *x, const float *xs, const uint8_
     p.spin_limit = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
     p.system_scope = scope == AREPI_SCOPE_SYSTEM;
     p.consume = (tile_cfg & AREPI_TILE_CONSUME_READY) ? 1 : 0;
-    rc = plan(p, find_tile(AREPI_TILE_256x128_S3), M, N, K, R, owner, flag_tile_m, flag_tile_n,
+    rc = plan(p, find_tile(AREPI_TILE_256x256_W8_K64), M, N, K, R, owner, flag_tile_m, flag_tile_n,
               publish || p.consume, /*contiguous=*/true);
     if (rc) return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

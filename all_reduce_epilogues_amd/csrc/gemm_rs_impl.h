@@ -524,11 +524,12 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         // on the 64-wide fp8 MFMA into the one accumulator set, which carries
         // the running sum rescaled: after block b, acc *= s_b / s_{b+1}
         // (s_b = xs[m,b] * ws[n/128,b]), and after the last block acc *=
-        // s_last, so acc ends at sum_b s_b * d_b.  The tile's columns lie in
-        // one 128-column scale block (BN == 128, n0 a multiple of 128).  The
-        // kernel allocates, past the stages, S scale areas of 2 KiB and 2*BM
-        // floats of per-row factors.
-        static_assert(BN == 128, "one W scale block per tile");
+        // s_last, so acc ends at sum_b s_b * d_b.  The tile spans NCB
+        // 128-column scale blocks (n0 a multiple of 128) and each wave's
+        // columns lie in one of them.  The kernel allocates, past the stages, S
+        // scale areas of 2 KiB and 2*NCB*BM floats of factors.
+        constexpr int NCB = BN / 128;
+        static_assert(NCB * 128 == BN && 128 % WN == 0, "a wave's columns lie in one W scale block");
         // Chunk c of tile row v sits at c ^ swz8(v).  Two 128-byte rows share a
         // 256-byte line of the 64 banks; ((v >> 1) & 7) sends the 16 rows of
         // one parity to 8 positions twice each, so the 16-byte operand reads of
@@ -568,17 +569,20 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         }
         // Scales ride one block ahead: the loads of step kt bring block kt+1's
         // scales into stage kt's scale area -- waves 0..3 the row scales of
-        // tile rows 64*wave + lane (slot = tile row), wave 4 lane 0 the
-        // column scale (slot 256); every other lane reads nothing (zeros).
+        // tile rows 64*wave + lane (slot = tile row), wave 4 lane c the
+        // column scale of the tile's scale block c (slot 256 + c); every other
+        // lane, and scale blocks past N, read nothing (zeros).
+        const int NBW = (int)((N + 127) / 128);
         const i32x4 sr = wave_u < 4 ? xsr : wsr;
         uint32_t so;
         {
             const int64_t gm = wave < 4 ? row_of(wave * 64 + lane) : -1;
             so = wave < 4 ? (gm >= 0 ? (uint32_t)(gm * KB * 4) : kOob)
-                          : (wave == 4 && lane == 0 ? (uint32_t)((int64_t)nb * KB * 4) : kOob);
+                          : (wave == 4 && lane < NCB && nb + lane < NBW ? (uint32_t)((int64_t)(nb + lane) * KB * 4)
+                                                                       : kOob);
         }
         lds_t *const SC = S0 + LDS_BYTES;                                   // [S][SCL]
-        float *const fac = reinterpret_cast<float *>(smem + LDS_BYTES + S * SCL);  // [2][BM]
+        float *const fac = reinterpret_cast<float *>(smem + LDS_BYTES + S * SCL);  // [2][NCB][BM]
         auto dma4 = [](i32x4 rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
             asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                          :
@@ -604,34 +608,36 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
             dma4(sr, __builtin_amdgcn_readfirstlane(lds_addr(SC + (kt % S) * SCL) + wave_u * 256), sin ? so : kOob,
                  __builtin_amdgcn_readfirstlane(sin ? (uint32_t)(kt + 1) * 4u : 0u));
         };
-        // Factors: thread t < BM keeps its row's current scale s_b and column
-        // scale in registers; at the top of step b it reads block b+1's from
-        // the scale area of stage b%S (landed with step b's operands) and
-        // writes the factor applied after block b, s_b/s_{b+1} (or s_last
-        // after the last block), into fac buffer b&1; the barrier that ends the
-        // step publishes it.  One division per row and block.  Rows past the
-        // end get factor 1 (their products are zero).
+        // Factors: thread t < BM keeps its row's current scale s_b and the
+        // column scales in registers; at the top of step b it reads block
+        // b+1's from the scale area of stage b%S (landed with step b's
+        // operands) and writes the factors applied after block b, s_b/s_{b+1}
+        // (or s_last after the last block), one per scale block, into fac
+        // buffer b&1; the barrier that ends the step publishes them.  One
+        // division per row, scale block and K block.  Rows past M and scale
+        // blocks past N get factor 1 (their products are zero).
         const int64_t frow = tid < BM ? row_of(tid) : -1;
         float rs = frow >= 0 ? p.xs[frow * KB] : 1.0f;
-        float cs = p.ws[(int64_t)nb * KB];
-        asm volatile("" ::"v"(rs), "v"(cs));  // both loads land before the first direct-to-LDS load is issued
+        float cs[NCB];
+#pragma unroll
+        for (int c = 0; c < NCB; ++c) cs[c] = nb + c < NBW ? p.ws[(int64_t)(nb + c) * KB] : 1.0f;
+        asm volatile("" ::"v"(rs), "v"(cs[0]), "v"(cs[NCB - 1]));  // the loads land before the first direct-to-LDS load
         auto write_factor = [&](int b) {
             if (tid < BM) {
-                float f;
-                if (b + 1 < KB) {
-                    const float *sc = reinterpret_cast<const float *>(smem + LDS_BYTES + (b % S) * SCL);
-                    const float rn = frow >= 0 ? sc[tid] : 1.0f, cn = sc[256];
-                    f = (rs / rn) * (cs / cn);
-                    rs = rn;
-                    cs = cn;
-                } else {
-                    f = rs * cs;
+                const float *sc = reinterpret_cast<const float *>(smem + LDS_BYTES + (b % S) * SCL);
+                const bool more = b + 1 < KB;
+                const float rn = more && frow >= 0 ? sc[tid] : 1.0f;
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) {
+                    const float cn = more && nb + c < NBW ? sc[256 + c] : 1.0f;
+                    fac[((b & 1) * NCB + c) * BM + tid] = more ? (rs / rn) * (cs[c] / cn) : rs * cs[c];
+                    cs[c] = cn;
                 }
-                fac[(b & 1) * BM + tid] = f;
+                rs = rn;
             }
         };
         auto apply_factor = [&](int b) {
-            const float *fb = fac + (b & 1) * BM;
+            const float *fb = fac + ((b & 1) * NCB + (wn * WN) / 128) * BM;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll

@@ -331,7 +331,7 @@ def gemm_rs_fp8_prestaged(A, inputs, torch, steps, warmup):
     ms = s.elapsed_time(e) / steps
     flops = 2.0 * M * N * K
     byts = M * K + N * K + 4.0 * (M + N // 128) * (K // 128) + 2.0 * ((R - 1) * seg * N + seg * N + (M - seg) * N)
-    return dict(M=M, N=N, K=K, R=R, tile="256x128", ms=ms, tflops=flops / ms / 1e9,
+    return dict(M=M, N=N, K=K, R=R, tile="256x256", ms=ms, tflops=flops / ms / 1e9,
                 frac_mfma_fp8=flops / ms / 1e9 / PEAK_FP8_TFLOPS, gbs=byts / ms / 1e6,
                 frac_hbm=byts / ms / 1e6 / PEAK_HBM_GBS)
 
