@@ -8,9 +8,9 @@
 // finding that the gfx950 matrix atom reads the OCP e4m3fn encoding (e4m3fnuz
 // bytes are not accepted).  The reduce-scatter epilogue is the direct-sum form
 // of gemm_rs.hip; the mainloop is the fp8 branch of the shared body
-// (gemm_rs_impl.h), on a 256x128 tile of eight 64x64 waves (per MFMA a 64x64
-// wave reads half the LDS bytes a 64x32 wave does; the taller tile loads a
-// quarter fewer operand bytes per FLOP than 128x128).
+// (gemm_rs_impl.h), on a 256x256 tile of eight 128x64 waves (one workgroup per
+// CU; per MFMA a 128x64 wave reads a third fewer LDS bytes than a 64x64 one,
+// and the wide tile loads half the operand bytes per FLOP of 128x128).
 #include "gemm_rs_impl.h"
 
 namespace arepi {

@@ -205,8 +205,8 @@ int arepi_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const uint16_t *con
  *   ws  fp32 [ceil(N/128)][K/128]     row-major; must be > 0 and finite
  * The reduce-scatter epilogue and every other argument are those of
  * arepi_gemm_rs_fused (direct sum over the R-1 peers).  The compute tile is
- * 256x128 (tile_cfg may only carry AREPI_TILE_CONSUME_READY; with ready_out,
- * flag tiles must nest inside 256x128 tiles).  Constraints:
+ * 256x256 (tile_cfg may only carry AREPI_TILE_CONSUME_READY; with ready_out,
+ * flag tiles must nest inside 256x256 tiles).  Constraints:
  * those of arepi_gemm_rs_fused plus K % 128 == 0; xs 4-byte aligned.
  * e4m3fnuz bytes are not this encoding (the same bits decode to other values).
  * ------------------------------------------------------------------------ */
