@@ -278,3 +278,24 @@ def test_ring_rejects_unaligned_segments_and_bad_pointers():
     rc = L.arepi_gemm_rs_ring(p, p, ctypes.cast(up, vp), p, p, p, None, 256, 512, 256, 4, 1, 128, 128,
                               3, 0, None, 0, None)
     assert rc == A.EINVAL and "scope=3" in A.last_error()
+
+
+@pytest.mark.parametrize("M,N,R,ftm,ftn", [
+    (256, 512, 2, 128, 128), (1024, 7168, 8, 128, 128), (4096, 4096, 4, 128, 128),
+    (200, 520, 2, 32, 64), (512, 512, 2, 256, 256), (512, 384, 2, 128, 128), (1024, 1024, 4, 64, 256),
+])
+def test_fp8_supports_nests_flag_tiles_in_its_256x256_tile(M, N, R, ftm, ftn):
+    K = 256
+    rc = A.gemm_rs_fp8_supports(M, N, K, R, 0, ftm, ftn, publish=True)
+    assert (rc == 0) == nests(M, N, R, ftm, ftn, 256, 256), A.last_error()
+    rc = A.gemm_rs_fp8_supports(M, N, K, R, 0, ftm, ftn, publish=False, tile=A.TILE_CONSUME_READY)
+    assert (rc == 0) == nests(M, N, R, ftm, ftn, 256, 256), A.last_error()
+    assert A.gemm_rs_fp8_supports(M, N, K, R, 0, ftm, ftn, publish=False) == 0
+
+
+def test_fp8_supports_rejects_k_and_tile_options():
+    assert A.gemm_rs_fp8_supports(512, 512, 192, 2, 0) != 0
+    assert "multiple of 128" in A.last_error()
+    assert A.gemm_rs_fp8_supports(512, 512, 256, 2, 0, tile=A.TILE_256x256_W8_K64) != 0
+    assert A.gemm_rs_fp8_supports(512, 512, 256, 2, 0, tile=A.TILE_PAIRED_ROWS) != 0
+    assert A.gemm_rs_fp8_supports(512, 512, 256, 2, 0, tile=A.TILE_CONSUME_READY) == 0
