@@ -609,12 +609,13 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                  __builtin_amdgcn_readfirstlane(sin ? (uint32_t)(kt + 1) * 4u : 0u));
         };
         // Factors: thread t < BM keeps its row's current scale s_b and the
-        // column scales in registers; at the top of step b it reads block
-        // b+1's from the scale area of stage b%S (landed with step b's
-        // operands) and writes the factors applied after block b, s_b/s_{b+1}
-        // (or s_last after the last block), one per scale block, into fac
-        // buffer b&1; the barrier that ends the step publishes them.  One
-        // division per row, scale block and K block.  Rows past M and scale
+        // column scales in registers; in step b (after issuing the next
+        // step's loads) it reads block b+1's from the scale area of stage b%S
+        // (landed with step b's operands) and writes the factors applied after
+        // block b, s_b/s_{b+1} (or s_last after the last block), one per scale
+        // block, into fac buffer b&1; the barrier that ends the step publishes
+        // them.  One reciprocal per row and K block and one per scale block.
+        // Rows past M and scale
         // blocks past N get factor 1 (their products are zero).
         const int64_t frow = tid < BM ? row_of(tid) : -1;
         float rs = frow >= 0 ? p.xs[frow * KB] : 1.0f;
@@ -627,10 +628,12 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                 const float *sc = reinterpret_cast<const float *>(smem + LDS_BYTES + (b % S) * SCL);
                 const bool more = b + 1 < KB;
                 const float rn = more && frow >= 0 ? sc[tid] : 1.0f;
+                // ratios through v_rcp_f32 (within 1 ulp; exact for powers of two)
+                const float rr = more ? rs * __builtin_amdgcn_rcpf(rn) : rs;
 #pragma unroll
                 for (int c = 0; c < NCB; ++c) {
                     const float cn = more && nb + c < NBW ? sc[256 + c] : 1.0f;
-                    fac[((b & 1) * NCB + c) * BM + tid] = more ? (rs / rn) * (cs[c] / cn) : rs * cs[c];
+                    fac[((b & 1) * NCB + c) * BM + tid] = rr * (more ? cs[c] * __builtin_amdgcn_rcpf(cn) : cs[c]);
                     cs[c] = cn;
                 }
                 rs = rn;
@@ -653,8 +656,8 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         __syncthreads();
         for (int b = 0; b < KB; ++b) {
             // stage b%S holds block b's operands and block b+1's scales
-            write_factor(b);
             issue8(b + S - 1);  // into stage (b-1)%S, free since the barrier that ended step b-1
+            write_factor(b);    // (reads stage b%S's scales, which issue8 does not touch)
             const lds_t *As = S0 + (b % S) * ST8;
             const lds_t *Bs = As + A8;
             // Two 64-wide MFMA steps per block (v_mfma_scale_f32_32x32x64_f8f6f4
