@@ -81,9 +81,9 @@ __device__ void copy_item(const EmuParams &p, const int64_t item) {
 // lands batches g, g + G, g + 2G, ... (G = grid size), so a grid smaller than
 // the batch count paces the landing like a link of bounded rate.  Each batch:
 // copies, drain, barrier, one release, then its bits.
-// Its waves must find room on CUs that hold the GEMM it feeds (whose owner
-// tiles spin on these bits): 73 VGPRs here against the 80 per SIMD lane that
-// two waves of the 214-VGPR headline GEMM tile leave free.
+// Its waves share CUs with the GEMM it feeds, whose owner tiles spin on these
+// bits: 73 VGPRs here, and two waves of the 214-VGPR headline GEMM tile leave
+// 80 per SIMD lane.
 __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
     const int64_t K = p.per_release, batches = (p.n_items + K - 1) / K;
     for (int64_t j = blockIdx.x; j < batches; j += gridDim.x) {
