@@ -19,6 +19,21 @@ int ok() {
     return AREPI_OK;
 }
 
+int64_t default_spin_bound() {
+    // one second of the device's constant-rate clock, read once per device
+    // (100 MHz assumed if the runtime cannot say)
+    constexpr int kMaxDevices = 64;
+    static int64_t ticks[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -int64_t(100000000);
+    if (ticks[dev] == 0) {
+        int khz = 0;
+        const bool known = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0;
+        ticks[dev] = known ? int64_t(khz) * 1000 : int64_t(100000000);
+    }
+    return -ticks[dev];
+}
+
 int check_launch(const char *what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -22,10 +22,22 @@ int check_launch(const char *what);
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Default number of polls of a bounded wait (each poll sleeps ~100 ns).
-constexpr int64_t kDefaultSpinLimit = int64_t(1) << 24;
+// Bound of a spin wait as passed to the kernels: > 0 is a number of polls;
+// < 0 is a wall-clock budget of -bound ticks of the device's constant-rate
+// clock (s_memrealtime).  default_spin_bound() is about one second of that
+// clock on the current device (its rate read once per device).
+int64_t default_spin_bound();
+inline int64_t spin_bound(int64_t spin_limit) { return spin_limit > 0 ? spin_limit : default_spin_bound(); }
 
 // ---- device-side helpers ------------------------------------------------------
+
+// One step of a bounded wait started at wall-clock time t0: true when the
+// bound (spin_bound's encoding) is used up; n counts the polls.
+__device__ __forceinline__ uint64_t spin_clock() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ bool spin_expired(int64_t bound, int64_t &n, uint64_t t0) {
+    if (bound > 0) return ++n > bound;
+    return (int64_t)(spin_clock() - t0) > -bound;
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

@@ -96,7 +96,7 @@ extern "C" int arepi_gemm_rs_fp8(const uint8_t *x, const float *xs, const uint8_
     p.send = send;
     p.ready_out = ready_out;
     p.status = status;
-    p.spin_limit = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
+    p.spin_limit = spin_bound(spin_limit);
     p.system_scope = scope == AREPI_SCOPE_SYSTEM;
     p.consume = (tile_cfg & AREPI_TILE_CONSUME_READY) ? 1 : 0;
     rc = plan(p, find_tile(AREPI_TILE_256x256_W8_K64), M, N, K, R, owner, flag_tile_m, flag_tile_n,

@@ -167,6 +167,7 @@ __global__ void __launch_bounds__(NT) ar_rmsnorm_kernel(uint16_t *__restrict__ s
     // Slow pass: packs that had not fully landed, redone in slot order.
     if (bad) {
         int64_t spins = 0;
+        const uint64_t t0 = spin_clock();
         bool gave_up = false;
 #pragma unroll
         for (int j = 0; j < PPT; ++j) {
@@ -178,7 +179,7 @@ __global__ void __launch_bounds__(NT) ar_rmsnorm_kernel(uint16_t *__restrict__ s
                 uint64_t *p64 = reinterpret_cast<uint64_t *>(base + (int64_t)sl * M * N);
                 uint64_t lo = load64_coherent(p64, sys), hi = load64_coherent(p64 + 1, sys);
                 while (!gave_up && (has_sentinel(lo) || has_sentinel(hi))) {
-                    if (++spins > spin_limit) {
+                    if (spin_expired(spin_limit, spins, t0)) {
                         gave_up = true;
                         if (status) atomicOr(status, (uint32_t)AREPI_STATUS_TIMEOUT);
                         break;
@@ -353,8 +354,9 @@ __global__ void __launch_bounds__(NT) lamport2_kernel(const Lamport2Params p) {
                 uint16_t *base = mine + row * p.N + (int64_t)(tid + j * NT) * 8;
                 uint64_t *p64 = reinterpret_cast<uint64_t *>(base);
                 uint64_t lo = load64_coherent(p64, sys), hi = load64_coherent(p64 + 1, sys);
+                const uint64_t t0 = spin_clock();
                 while (!gave_up && (has_sentinel(lo) || has_sentinel(hi))) {
-                    if (++spins > p.spin_limit) {
+                    if (spin_expired(p.spin_limit, spins, t0)) {
                         gave_up = true;
                         if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
                         break;
@@ -474,7 +476,7 @@ extern "C" int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma
     if (M * N * 2 * 8 > (int64_t)1 << 31)
         return fail(AREPI_EUNSUPPORTED, "arepi_ar_rmsnorm_lamport: one staging slot (M*N*2 bytes) must be at most 256 MiB");
     const int64_t packs = N / 8;
-    const int64_t lim = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
+    const int64_t lim = spin_bound(spin_limit);
     const int sys = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int ppt = (int)((packs + 255) / 256);
@@ -537,7 +539,7 @@ extern "C" int arepi_ar_rmsnorm_lamport_2phase(const uint16_t *const *inputs, ui
     p.out = out;
     p.status = status;
     p.eps = eps;
-    p.spin_limit = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
+    p.spin_limit = spin_bound(spin_limit);
     p.phase_b = 1;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int64_t packs = N / 8;
