@@ -70,6 +70,7 @@ def lib():
             "arepi_gemm_rs_fused": ([vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
                                      u32p, i64, vp], i32),
             "arepi_gemm_rs_ring_supports": ([i64, i64, i64, i32, i32, i32, i32, i32, i32], i32),
+            "arepi_gemm_rs_ring_pick_tile": ([i64, i64, i64, i32, i32, i32, i32, i32], i32),
             "arepi_gemm_rs_ring": ([vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32,
                                     u32p, i64, vp], i32),
             "arepi_gemm_rs_fp8_supports": ([i64, i64, i64, i32, i32, i32, i32, i32, i32], i32),
@@ -219,6 +220,11 @@ def gemm_rs_ring_supports(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, p
                           tile=TILE_AUTO) -> int:
     """0 when the push-ring form supports the shape, else the negative status."""
     return lib().arepi_gemm_rs_ring_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish), tile)
+
+
+def gemm_rs_ring_pick_tile(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publish=False) -> int:
+    return _check(lib().arepi_gemm_rs_ring_pick_tile(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish)),
+                  "gemm_rs_ring_pick_tile")
 
 
 def gemm_rs_ring(x, w, upstream, ready_in, out, send, R: int, owner: int, ready_out=None,

@@ -137,7 +137,7 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
     p.send = send;
     p.ready_out = ready_out;
     p.status = status;
-    p.spin_limit = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
+    p.spin_limit = spin_bound(spin_limit);
     p.system_scope = scope == AREPI_SCOPE_SYSTEM;
     p.consume = c.consume ? 1 : 0;
     rc = plan(p, c.t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous);

@@ -69,7 +69,7 @@ struct GemmRsParams {
     int64_t M, N, K, seg;
     int64_t ftiles_n;  // flag tiles per segment row band
     int64_t fwords;    // u32 words per peer
-    int64_t spin_limit;
+    int64_t spin_limit;  // bound of each wait: > 0 polls, < 0 ticks of the wall clock
     int R, owner, ftm, ftn;
     int system_scope;
     int nRB, nCB, ob1, group, xcd_chunk, nWG;
@@ -728,6 +728,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     for (int h = 0; h < 2; ++h) has_other |= r0[h] < r1[h] && (r0[h] < oseg0 || r1[h] > oseg1);
     const int tc0 = (int)(n0 / p.ftn), ntc = (int)((min(n0 + BN, N) - 1) / p.ftn) - tc0 + 1;
 
+    auto wait_ready = [&]() {
     if constexpr (has_owner) {
         // Wait until every flag tile this tile adds is set: one (source, flag
         // tile) item per lane, all polled at once with relaxed loads, then one
@@ -738,11 +739,12 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         if (wave == 0) {
             auto wait_items = [&](int items, auto item) {
                 int64_t spins = 0;
+                const uint64_t t0 = spin_clock();
                 for (int k = lane; k < items; k += 64) {
                     uint32_t *word, bit;
                     item(k, word, bit);
                     while (!(load_relaxed(word, sys) & bit)) {
-                        if (++spins > p.spin_limit) {
+                        if (spin_expired(p.spin_limit, spins, t0)) {
                             if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
                             break;
                         }
@@ -812,6 +814,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         }
         __syncthreads();
     }
+    };
 
     // Peer combine on the matrix cores.  For every 32-row accumulator block
     // holding owner rows, each peer's partial P (bf16, ascending rank order) is
@@ -957,11 +960,19 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                                                             valid ? recv_bytes : 0, kBufferDword3);
             pneg[sl] = (kRingK || valid) ? 0u : 0x80008000u;
         }
-#pragma unroll
-        for (int ou = 0; ou < D; ++ou) prefetch(ou);
     }
+    // the first D units' peer packs (after the readiness wait)
+    auto start_prefetch = [&]() {
+        if constexpr (NOU > 0) {
+#pragma unroll
+            for (int ou = 0; ou < D; ++ou) prefetch(ou);
+        }
+    };
     // Drain block i; `c` is its index among the owner-candidate blocks, or -1.
-    auto drain_block = [&](int i, int c) {
+    // `rows` selects the rows stored: kAllRows, kOtherRows (rows outside the
+    // owner segment, no peers added) or kOwnRows (owner rows only).
+    enum { kAllRows = 0, kOtherRows = 1, kOwnRows = 2 };
+    auto drain_block = [&](int i, int c, int rows) {
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             // accumulator register r of a 32x32 tile holds row 8*(r/4) + 4*(lane/32) + r%4
@@ -1008,28 +1019,18 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                 const i32x4 qv = {(int)q8.x, (int)q8.y, (int)q8.z, (int)q8.w};
                 if constexpr (has_owner)
                     __builtin_amdgcn_raw_buffer_store_b128(
-                        qv, out_rs, (ok && own) ? (uint32_t)((row0 - oseg0) * N2 + lane_off) : kOob, 0,
-                        kAuxNontemporal);
+                        qv, out_rs, (ok && own && rows != kOtherRows) ? (uint32_t)((row0 - oseg0) * N2 + lane_off) : kOob,
+                        0, kAuxNontemporal);
                 __builtin_amdgcn_raw_buffer_store_b128(
-                    qv, send_rs, (ok && !own) ? (uint32_t)(row0 * N2 + lane_off) : kOob, 0, kAuxNontemporal);
+                    qv, send_rs, (ok && !own && rows != kOwnRows) ? (uint32_t)(row0 * N2 + lane_off) : kOob, 0,
+                    kAuxNontemporal);
             }
         }
     };
 
-    if constexpr (kAOnly) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-            if (!block_is_a(i)) drain_block(i, -1);
-#pragma unroll
-        for (int c = 0; c < NOB; ++c) drain_block(cand_block(c), c);
-    } else {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) drain_block(i, KIND == kNoOwnerRows ? -1 : i);
-    }
-
     // Publish the send tiles: drain this thread's stores, balanced barrier, one
     // release, then relaxed bit sets.
-    if (p.ready_out && has_other) {
+    auto publish = [&]() {
         drain_stores();
         __syncthreads();
         if (wave == 0) {
@@ -1052,6 +1053,58 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                 }
             }
         }
+    };
+    const bool publishes = p.ready_out && has_other;
+
+    // A tile with owner rows and rows of other segments publishes the other
+    // segments' rows before it waits: across ranks, a wait placed before that
+    // publication could close a cycle (this rank's owner rows waiting on a
+    // peer whose own such tile waits on this rank's publication).  Its
+    // accumulators are staged twice: other rows, publish, wait, owner rows.
+    if constexpr (kRingK) {
+        // (the ring refuses tiles that span segments when it publishes)
+        wait_ready();
+        start_prefetch();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) drain_block(i, i, kAllRows);
+        if (publishes) publish();
+    } else if constexpr (kAOnly) {
+        // chunk B holds no owner rows, chunk A only owner rows
+        if (publishes) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                if (!block_is_a(i)) drain_block(i, -1, kAllRows);
+            publish();
+            wait_ready();
+            start_prefetch();
+        } else {
+            wait_ready();
+            start_prefetch();
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                if (!block_is_a(i)) drain_block(i, -1, kAllRows);
+        }
+#pragma unroll
+        for (int c = 0; c < NOB; ++c) drain_block(cand_block(c), c, kAllRows);
+    } else if constexpr (has_owner) {
+        if (publishes) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) drain_block(i, -1, kOtherRows);
+            publish();
+            wait_ready();
+            start_prefetch();
+#pragma unroll
+            for (int i = 0; i < TM; ++i) drain_block(i, i, kOwnRows);
+        } else {
+            wait_ready();
+            start_prefetch();
+#pragma unroll
+            for (int i = 0; i < TM; ++i) drain_block(i, i, kAllRows);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) drain_block(i, -1, kAllRows);
+        if (publishes) publish();
     }
 }
 
@@ -1134,12 +1187,15 @@ bool use_paired(int64_t M, int64_t N, int R, int ftm, int ftn, int BM, int BN, b
     return !publish || flags_nest(M, N, R, ftm, ftn, CK, BN);
 }
 
-int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool publish) {
+// whole_segments: only tiles whose row blocks each lie in one segment (the
+// push ring's condition for publishing).
+int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool publish, bool whole_segments = false) {
     (void)K;
     int best = -1;
     double best_cost = 0;
     for (const auto &t : kTiles) {
         if (publish && !flags_nest(M, N, R, ftm, ftn, t.BM, t.BN)) continue;
+        if (whole_segments && R > 1 && (M / R) % t.BM) continue;
         const int64_t count = cdiv(M, t.BM) * cdiv(N, t.BN);
         // waves of co-resident tiles x time of one wave; a wave with fewer
         // tiles than slots on each CU runs fewer of them side by side
@@ -1196,13 +1252,14 @@ struct CfgChoice {
     int id;
     bool contiguous, consume, nest;
 };
-CfgChoice decode_cfg(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool publish, int tile_cfg) {
+CfgChoice decode_cfg(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool publish, int tile_cfg,
+                     bool whole_segments = false) {
     CfgChoice c{};
     c.consume = (tile_cfg & AREPI_TILE_CONSUME_READY) != 0;
     c.nest = publish || c.consume;
     c.contiguous = (tile_cfg & AREPI_TILE_PAIRED_ROWS) == 0;
     const int id = tile_cfg & ~(AREPI_TILE_PAIRED_ROWS | AREPI_TILE_CONSUME_READY);
-    c.id = id == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, ftm, ftn, c.nest) : id;
+    c.id = id == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, ftm, ftn, c.nest, whole_segments && publish) : id;
     c.t = find_tile(c.id);
     return c;
 }

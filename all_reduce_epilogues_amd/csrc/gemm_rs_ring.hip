@@ -72,7 +72,33 @@ extern "C" int arepi_gemm_rs_ring_supports(int64_t M, int64_t N, int64_t K, int 
     if (R > 1 && (M / R) % kRingRowAlign)
         return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_ring: segment height M/R=" + std::to_string(M / R) +
                                             " must be a multiple of " + std::to_string(kRingRowAlign));
+    // When it publishes, a tile waits for its segments' upstream partials
+    // before it publishes them on; a tile spanning two segments would make each
+    // segment's publication wait for the other's arrival, which across the
+    // ranks of a ring closes a cycle.  So each row block must lie in one
+    // segment (the segment height a multiple of the tile height).
+    if (publish && R > 1) {
+        const int id = tile_cfg & ~AREPI_TILE_CONSUME_READY;
+        if (id == AREPI_TILE_AUTO) {
+            if (pick_tile(M, N, K, R, flag_tile_m, flag_tile_n, true, true) < 0)
+                return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_ring: no compute tile fits whole in one segment of " +
+                                                    std::to_string(M / R) + " rows with whole flag tiles");
+        } else if ((M / R) % find_tile(id)->BM) {
+            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_ring: with ready_out, tile rows " +
+                                                std::to_string(find_tile(id)->BM) + " must divide the segment height " +
+                                                std::to_string(M / R));
+        }
+    }
     return ok();
+}
+
+extern "C" int arepi_gemm_rs_ring_pick_tile(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
+                                            int flag_tile_n, int publish) {
+    int rc = arepi_gemm_rs_ring_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish, AREPI_TILE_AUTO);
+    if (rc) return rc;
+    const int t = pick_tile(M, N, K, R, flag_tile_m, flag_tile_n, publish != 0, publish != 0);
+    ok();
+    return t;
 }
 
 extern "C" int arepi_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const uint16_t *const *upstream,
@@ -102,7 +128,7 @@ extern "C" int arepi_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const ui
         if (!upstream[d]) return bad("upstream[" + std::to_string(d) + "] is NULL");
         if (!aligned16(upstream[d])) return bad("upstream[" + std::to_string(d) + "] must be 16-byte aligned");
     }
-    const CfgChoice c = decode_cfg(M, N, K, R, flag_tile_m, flag_tile_n, publish, tile_cfg);
+    const CfgChoice c = decode_cfg(M, N, K, R, flag_tile_m, flag_tile_n, publish, tile_cfg, /*whole_segments=*/true);
 
     GemmRsParams p{};
     p.x = x;
@@ -114,7 +140,7 @@ extern "C" int arepi_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const ui
     p.send = send;
     p.ready_out = ready_out;
     p.status = status;
-    p.spin_limit = spin_limit > 0 ? spin_limit : kDefaultSpinLimit;
+    p.spin_limit = spin_bound(spin_limit);
     p.system_scope = scope == AREPI_SCOPE_SYSTEM;
     p.consume = c.consume ? 1 : 0;
     rc = plan(p, c.t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, /*contiguous=*/true);

@@ -26,9 +26,11 @@
  *     default stream).  Device-side status words are read by the caller after
  *     synchronising.  The library allocates no device memory and keeps no state
  *     besides the per-thread error message.
- *   - Spin waits are bounded: `spin_limit` is the number of polls before a wait
- *     gives up (<= 0 selects about one second of polling); a wait that gives up
- *     ORs AREPI_STATUS_TIMEOUT into *status (when status is non-NULL) and the
+ *   - Spin waits are bounded: `spin_limit` > 0 is the number of polls before a
+ *     wait gives up; <= 0 selects a deadline of one second of the device's
+ *     constant-rate wall clock (s_memrealtime, its rate read from the runtime)
+ *     from the start of the wait.  A wait that gives up ORs
+ *     AREPI_STATUS_TIMEOUT into *status (when status is non-NULL) and the
  *     kernel finishes normally, with the affected outputs unspecified.
  */
 #ifndef AREPI_H
@@ -120,7 +122,10 @@ const char *arepi_version(void);
  *            flag tile of every non-owner segment has its bit set, each set
  *            with a release at `scope` once that tile's send rows are stored.
  *   status   device u32 or NULL; spin_limit as above.
- * Owner tiles wait for their ready_in bits with an acquire at `scope`.
+ * Owner tiles wait for their ready_in bits with an acquire at `scope`.  A
+ * workgroup holding owner rows and rows of other segments stores and publishes
+ * those other rows before it waits (a wait ahead of that publication could
+ * close a cycle across ranks whose such workgroups wait on each other).
  * Constraints: 1 <= R <= 8, 0 <= owner < R, M % R == 0, M >= 1, N >= 8,
  * N % 8 == 0, K >= 8, K % 8 == 0, flag tiles >= 1x1.  With ready_out, flag
  * tiles must nest inside the compute tiles (see arepi_gemm_rs_supports).
@@ -179,10 +184,20 @@ int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const uint16_t *co
  * acquire at `scope`.  Tiles run segment by segment in ring order: chain first,
  * then chain-1, ..., owner last.
  * Constraints: those of arepi_gemm_rs_fused, plus (M/R) % 8 == 0 when R > 1;
- * AREPI_TILE_PAIRED_ROWS is refused (EUNSUPPORTED).
+ * AREPI_TILE_PAIRED_ROWS is refused (EUNSUPPORTED).  With ready_out, every row
+ * block must lie in one segment (tile rows dividing M/R): a tile publishes a
+ * segment only after that segment's upstream partial arrived, so a tile over
+ * two segments would hold each publication behind the other's arrival, a
+ * cycle across the ranks of a ring (EUNSUPPORTED otherwise).
  * ------------------------------------------------------------------------ */
 int arepi_gemm_rs_ring_supports(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
                                 int flag_tile_n, int publish, int tile_cfg);
+
+/* Compute tile (AREPI_TILE_*) the automatic choice of arepi_gemm_rs_ring
+ * picks for a shape, or a negative status.  With publish set it only takes
+ * tiles whose row blocks each lie in one segment (see arepi_gemm_rs_ring). */
+int arepi_gemm_rs_ring_pick_tile(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
+                                 int flag_tile_n, int publish);
 
 int arepi_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const uint16_t *const *upstream,
                        uint32_t *ready_in, uint16_t *out, uint16_t *send, uint32_t *ready_out,

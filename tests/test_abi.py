@@ -244,12 +244,25 @@ def test_consume_option_plans_like_publication(M, N, R):
 @pytest.mark.parametrize("M,N,R,owner", [(256, 512, 2, 0), (4096, 4096, 4, 0), (256, 7168, 8, 0), (96, 72, 4, 2)])
 def test_ring_supports_follows_the_direct_form(M, N, R, owner):
     """The push-ring form accepts what the direct form accepts (contiguous
-    rows), refuses paired half-blocks, and needs 8-row-aligned segments."""
+    rows), refuses paired half-blocks, and needs 8-row-aligned segments; when
+    it publishes, every row block must also lie in one segment (tile rows
+    dividing M/R), and the automatic choice keeps to such tiles."""
+    seg = M // R
+    whole = [t for t in TILE_DIMS if seg % TILE_DIMS[t][0] == 0 and
+             A.gemm_rs_supports(M, N, 64, R, owner, 128, 128, publish=True, tile=t) == 0]
     for tile in TILE_DIMS:
         for publish in (False, True):
             d = A.gemm_rs_supports(M, N, 64, R, owner, 128, 128, publish=publish, tile=tile)
             r = A.gemm_rs_ring_supports(M, N, 64, R, owner, 128, 128, publish=publish, tile=tile)
-            assert r == d, (tile, publish, A.last_error())
+            if publish and R > 1 and d == 0 and seg % TILE_DIMS[tile][0]:
+                assert r == A.EUNSUPPORTED and "segment height" in A.last_error(), (tile, A.last_error())
+            else:
+                assert r == d, (tile, publish, A.last_error())
+    auto = A.gemm_rs_ring_supports(M, N, 64, R, owner, 128, 128, publish=True)
+    if R > 1 and seg % 8 == 0:
+        assert (auto == 0) == bool(whole), A.last_error()
+    if auto == 0 and R > 1:
+        assert A.gemm_rs_ring_pick_tile(M, N, 64, R, owner, publish=True) in whole
         assert A.gemm_rs_ring_supports(M, N, 64, R, owner, 128, 128, tile=tile | A.TILE_PAIRED_ROWS) == \
             A.EUNSUPPORTED
         assert "direct form only" in A.last_error()

@@ -123,13 +123,17 @@ def test_ragged_shapes_every_tile(M, N, K, R, owner, ftm, ftn):
 @pytest.mark.parametrize("owner", [0, 1])
 def test_two_ranks_ring_is_the_direct_sum_bit_for_bit(owner):
     """With R = 2 the ring hop and the direct sum do the same arithmetic on the
-    same accumulators: identical bits from the two GPU entry points."""
+    same accumulators: identical bits from the two GPU entry points on the same
+    compute tile (both calls without ready_out, so the automatic choice is the
+    same too).  The tiles cover the fold of the partial inside the K loop
+    (two-stage tiles) and the add after it (four-stage tiles)."""
     dev = device()
     M, N, K, R = 512, 1024, 512, 2
     case = inputs.gemm_rs_ring_case(M, N, K, R, owner=owner, seed=77)
     part = case["up"][owner]
-    for tile in (A.TILE_AUTO, A.TILE_128x128_S4, A.TILE_256x256_W8):
-        ring = run(case, tile=tile)
+    for tile in (A.TILE_AUTO, A.TILE_128x128_S4, A.TILE_256x256_W8, A.TILE_256x256_W8_K64, A.TILE_64x128,
+                 A.TILE_128x128):
+        ring = run(case, tile=tile, publish=False)
         recv = [None, None]
         recv[1 - owner] = to_dev_bf16(part)
         rin = to_dev_u32(ready_all(R, owner, oracle.flag_tiles(M, N, R, 128, 128)))
