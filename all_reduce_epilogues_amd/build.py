@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libarepi.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "gemm_rs.hip", "gemm_rs_ring.hip", "gemm_rs_fp8.hip", "lamport.hip", "combine.hip", "emu_producer.hip"]
+SOURCES = ["abi.cpp", "gemm_rs.hip", "gemm_rs_mixed.hip", "gemm_rs_ring.hip", "gemm_rs_fp8.hip", "lamport.hip", "combine.hip", "emu_producer.hip"]
 
 # -packed-fp32-ops is turned off for every device compile: the compiler still
 # vectorises, but never emits the packed fp32 add/mul/fma forms.

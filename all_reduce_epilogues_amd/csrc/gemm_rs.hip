@@ -8,49 +8,8 @@
 // segment's tiles add the R-1 peer partials in the epilogue, all other rows are
 // stored as this rank's outgoing partials.  The kernel body, tile schedule and
 // host-side planning are shared with the push-ring form (gemm_rs_impl.h).
-#include "gemm_rs_impl.h"
+#include "gemm_rs_kernel.h"
 
-namespace arepi {
-namespace {
-
-// WPE: waves per SIMD the register allocation targets (1 = one big-tile
-// workgroup per CU; 2 = two co-resident workgroups; 0 = no target).
-template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-    __attribute__((amdgpu_waves_per_eu(WPE > 0 ? WPE : 1, WPE > 0 ? WPE : 8)))
-    gemm_rs_kernel(const GemmRsParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<BM, BN, BK, S>()];
-    constexpr int CK = BM >= 64 ? BM / 2 : BM;
-    int rb, cb;
-    tile_of_block(p, blockIdx.x, rb, cb);
-    int64_t a0, b0;
-    int alen, blen;
-    chunks_of_block(p, BM, CK, rb, a0, alen, b0, blen);
-    const int64_t oseg0 = (int64_t)p.owner * p.seg, oseg1 = oseg0 + p.seg;
-    const bool own_a = alen > 0 && a0 < oseg1 && a0 + alen > oseg0;
-    const bool own_b = blen > 0 && b0 < oseg1 && b0 + blen > oseg0;
-    if (!own_a && !own_b)
-        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kNoOwnerRows>(p, smem, rb, cb, a0, alen, b0, blen);
-    else if (p.paired)  // paired half-blocks: only chunk A can be an owner chunk
-        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerChunkA>(p, smem, rb, cb, a0, alen, b0, blen);
-    else
-        gemm_rs_body<BM, BN, WM, WN, BK, S, WPE, PEERS, kOwnerRowsAnywhere>(p, smem, rb, cb, a0, alen, b0, blen);
-}
-
-template <int BM, int BN, int WM, int WN, int BK, int S, int WPE>
-void launch(const GemmRsParams &p, hipStream_t stream) {
-    constexpr int NT = (BM / WM) * (BN / WN) * 64;
-    if (p.npeers <= 1)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1>), dim3(p.nWG), dim3(NT), 0, stream, p);
-    else if (p.npeers <= 3)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3>), dim3(p.nWG), dim3(NT), 0, stream, p);
-    else
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1>), dim3(p.nWG), dim3(NT), 0,
-                           stream, p);
-}
-
-}  // namespace
-}  // namespace arepi
 
 using namespace arepi;
 
@@ -144,20 +103,13 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
     if (rc) return rc;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    switch (cfg) {
-        case AREPI_TILE_256x256: launch<256, 256, 128, 128, 64, 2, 1>(p, s); break;
-        case AREPI_TILE_128x256: launch<128, 256, 64, 128, 64, 2, 1>(p, s); break;
-        case AREPI_TILE_128x128: launch<128, 128, 64, 64, 64, 2, 0>(p, s); break;
-        case AREPI_TILE_64x128: launch<64, 128, 32, 64, 64, 2, 0>(p, s); break;
-        case AREPI_TILE_32x256: launch<32, 256, 32, 64, 64, 2, 0>(p, s); break;
-        case AREPI_TILE_256x256_S4: launch<256, 256, 128, 128, 32, 4, 1>(p, s); break;
-        case AREPI_TILE_256x128_S3: launch<256, 128, 128, 64, 32, 3, 2>(p, s); break;
-        case AREPI_TILE_128x256_S3: launch<128, 256, 64, 128, 32, 3, 2>(p, s); break;
-        case AREPI_TILE_128x128_S4: launch<128, 128, 64, 64, 32, 4, 2>(p, s); break;
-        case AREPI_TILE_256x256_W8: launch<256, 256, 128, 64, 32, 4, 2>(p, s); break;
-        case AREPI_TILE_256x256_W8_K64: launch<256, 256, 128, 64, 64, 2, 2>(p, s); break;
-        default: return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_fused: no kernel for tile " + std::to_string(cfg));
-    }
+    // a workgroup can mix owner rows with published rows of other segments
+    // only when ready_out is given and either half-blocks are paired or a row
+    // block straddles a segment boundary
+    const int BM = c.t->BM;
+    const bool mixed = ready_out && R > 1 && (p.paired || p.seg % BM != 0);
+    const bool launched = mixed ? launch_gemm_rs_mixed(cfg, &p, s) : launch_tile<false>(cfg, p, s);
+    if (!launched) return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_fused: no kernel for tile " + std::to_string(cfg));
     return check_launch("arepi_gemm_rs_fused");
 }
 

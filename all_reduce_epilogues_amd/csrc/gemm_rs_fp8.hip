@@ -16,7 +16,9 @@
 namespace arepi {
 namespace {
 
-template <int PEERS>
+// MIXED: the instantiation that can run a workgroup holding owner rows beside
+// published rows of other segments (published before its readiness wait).
+template <int PEERS, bool MIXED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_rs_fp8_kernel(const GemmRsParams p) {
     // two stages, their 2 KiB scale areas, then 2 x 2 x 256 factors
     __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<256, 256, 64, 2>() + 2 * 2048 + 2 * 2 * 256 * 4];
@@ -29,11 +31,20 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int64_t oseg0 = (int64_t)p.owner * p.seg, oseg1 = oseg0 + p.seg;
     const bool own_a = alen > 0 && a0 < oseg1 && a0 + alen > oseg0;
     const bool own_b = blen > 0 && b0 < oseg1 && b0 + blen > oseg0;
-    if (!own_a && !own_b)
+    if (!own_a && !own_b) {
         gemm_rs_body<256, 256, 128, 64, 64, 2, 2, PEERS, kNoOwnerRows, true>(p, smem, rb, cb, a0, alen, b0, blen);
-    else
-        gemm_rs_body<256, 256, 128, 64, 64, 2, 2, PEERS, kOwnerRowsAnywhere, true>(p, smem, rb, cb, a0, alen, b0,
-                                                                                 blen);
+        return;
+    }
+    if constexpr (MIXED) {
+        const bool other_a = alen > 0 && (a0 < oseg0 || a0 + alen > oseg1);
+        const bool other_b = blen > 0 && (b0 < oseg0 || b0 + blen > oseg1);
+        if (p.ready_out != nullptr && (other_a || other_b)) {
+            gemm_rs_body<256, 256, 128, 64, 64, 2, 2, PEERS, kOwnerAnywherePub, true>(p, smem, rb, cb, a0, alen, b0,
+                                                                                    blen);
+            return;
+        }
+    }
+    gemm_rs_body<256, 256, 128, 64, 64, 2, 2, PEERS, kOwnerRowsAnywhere, true>(p, smem, rb, cb, a0, alen, b0, blen);
 }
 
 }  // namespace
@@ -103,11 +114,22 @@ extern "C" int arepi_gemm_rs_fp8(const uint8_t *x, const float *xs, const uint8_
               publish || p.consume, /*contiguous=*/true);
     if (rc) return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (p.npeers <= 1)
-        hipLaunchKernelGGL(gemm_rs_fp8_kernel<1>, dim3(p.nWG), dim3(512), 0, s, p);
-    else if (p.npeers <= 3)
-        hipLaunchKernelGGL(gemm_rs_fp8_kernel<3>, dim3(p.nWG), dim3(512), 0, s, p);
-    else
-        hipLaunchKernelGGL(gemm_rs_fp8_kernel<kMaxR - 1>, dim3(p.nWG), dim3(512), 0, s, p);
+    // a 256-row block mixes owner rows with published rows only when ready_out
+    // is given and the segment height is not a multiple of 256
+    if (ready_out && R > 1 && p.seg % 256) {
+        if (p.npeers <= 1)
+            hipLaunchKernelGGL((gemm_rs_fp8_kernel<1, true>), dim3(p.nWG), dim3(512), 0, s, p);
+        else if (p.npeers <= 3)
+            hipLaunchKernelGGL((gemm_rs_fp8_kernel<3, true>), dim3(p.nWG), dim3(512), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_rs_fp8_kernel<kMaxR - 1, true>), dim3(p.nWG), dim3(512), 0, s, p);
+    } else {
+        if (p.npeers <= 1)
+            hipLaunchKernelGGL((gemm_rs_fp8_kernel<1, false>), dim3(p.nWG), dim3(512), 0, s, p);
+        else if (p.npeers <= 3)
+            hipLaunchKernelGGL((gemm_rs_fp8_kernel<3, false>), dim3(p.nWG), dim3(512), 0, s, p);
+        else
+            hipLaunchKernelGGL((gemm_rs_fp8_kernel<kMaxR - 1, false>), dim3(p.nWG), dim3(512), 0, s, p);
+    }
     return check_launch("arepi_gemm_rs_fp8");
 }

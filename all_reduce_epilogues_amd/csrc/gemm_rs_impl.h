@@ -204,7 +204,17 @@ constexpr int lds_bytes() { return S * (BM * BK * 2 + BK * BN * 2); }
 // all of them through vector registers).
 // kRing: push-ring form, every row outside the chain segment adds the
 // upstream partial of its own segment.
-enum { kNoOwnerRows = 0, kOwnerChunkA = 1, kOwnerRowsAnywhere = 2, kRing = 3 };
+// kOwnerChunkAPub, kOwnerAnywherePub: as kOwnerChunkA / kOwnerRowsAnywhere for
+// a tile that also holds rows of other segments and publishes them
+// (ready_out): those rows are stored and published before the readiness wait.
+enum {
+    kNoOwnerRows = 0,
+    kOwnerChunkA = 1,
+    kOwnerRowsAnywhere = 2,
+    kRing = 3,
+    kOwnerChunkAPub = 4,
+    kOwnerAnywherePub = 5
+};
 
 template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, int PEERS, int KIND, bool FP8 = false>
 __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *smem, int rb, int cb, int64_t a0,
@@ -869,7 +879,8 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     constexpr int UPB = NQ * STEPS; // units per 32-row block
     static_assert(STEPS >= 1 && STEPS * RPS == ER, "epilogue step split");
     static_assert(!kRingK || RPS <= 8, "ring units must fit the 8-row segment alignment");
-    constexpr bool kAOnly = KIND == kOwnerChunkA && kStaticHalves;
+    constexpr bool kPubFirst = KIND == kOwnerChunkAPub || KIND == kOwnerAnywherePub;
+    constexpr bool kAOnly = (KIND == kOwnerChunkA || KIND == kOwnerChunkAPub) && kStaticHalves;
     auto block_is_a = [](int i) { return !(((i * 32) / IL) & 1); };
     // owner-candidate blocks, in drain order
     constexpr int NOB = KIND == kNoOwnerRows ? 0 : kAOnly ? (TM + 1) / 2 : TM;
@@ -1057,10 +1068,10 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     const bool publishes = p.ready_out && has_other;
 
     // A tile with owner rows and rows of other segments publishes the other
-    // segments' rows before it waits: across ranks, a wait placed before that
-    // publication could close a cycle (this rank's owner rows waiting on a
-    // peer whose own such tile waits on this rank's publication).  Its
-    // accumulators are staged twice: other rows, publish, wait, owner rows.
+    // segments' rows before it waits (kPubFirst): across ranks, a wait placed
+    // before that publication could close a cycle (this rank's owner rows
+    // waiting on a peer whose own such tile waits on this rank's publication).
+    // Its accumulators are staged twice: other rows, publish, wait, owner rows.
     if constexpr (kRingK) {
         // (the ring refuses tiles that span segments when it publishes)
         wait_ready();
@@ -1070,7 +1081,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         if (publishes) publish();
     } else if constexpr (kAOnly) {
         // chunk B holds no owner rows, chunk A only owner rows
-        if (publishes) {
+        if constexpr (kPubFirst) {
 #pragma unroll
             for (int i = 0; i < TM; ++i)
                 if (!block_is_a(i)) drain_block(i, -1, kAllRows);
@@ -1086,21 +1097,21 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         }
 #pragma unroll
         for (int c = 0; c < NOB; ++c) drain_block(cand_block(c), c, kAllRows);
+        if (!kPubFirst && publishes) publish();
+    } else if constexpr (kPubFirst) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) drain_block(i, -1, kOtherRows);
+        publish();
+        wait_ready();
+        start_prefetch();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) drain_block(i, i, kOwnRows);
     } else if constexpr (has_owner) {
-        if (publishes) {
+        wait_ready();
+        start_prefetch();
 #pragma unroll
-            for (int i = 0; i < TM; ++i) drain_block(i, -1, kOtherRows);
-            publish();
-            wait_ready();
-            start_prefetch();
-#pragma unroll
-            for (int i = 0; i < TM; ++i) drain_block(i, i, kOwnRows);
-        } else {
-            wait_ready();
-            start_prefetch();
-#pragma unroll
-            for (int i = 0; i < TM; ++i) drain_block(i, i, kAllRows);
-        }
+        for (int i = 0; i < TM; ++i) drain_block(i, i, kAllRows);
+        if (publishes) publish();
     } else {
 #pragma unroll
         for (int i = 0; i < TM; ++i) drain_block(i, -1, kAllRows);

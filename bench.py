@@ -5,21 +5,29 @@ the tp=4 share -- X [4096,2048] . W [2048,4096] bf16, R=4, owner segment of 1024
 rows, three peer partials landed per 128x128 flag tile by an emulated-peer
 producer on a second stream in shuffled order, their ready bits published
 eight tiles per release -- as TFLOP/s of the whole step (2*M*N*K per step).
-The same step with one release per tile is reported beside it.  Inputs are
-resident in HBM before timing starts.
+The same step with one release per tile is reported beside it in `config`.
+Inputs are resident in HBM before timing starts.
 
-Also reported in the same run: the Lamport AR+RMSNorm consumer (8 x
-[4096,7168]) and the weighted top-8 combine ([4096,8,7168]) as GB/s of
-algorithmic bytes, each against the 8 TB/s HBM peak; the pre-staged tp=4
-kernel; the push-ring form of the same GEMM (one hop: the producer landing the
-upstream partials beside it, and pre-staged); the fp8 block-scaled form
-(pre-staged, against the fp8 peak); the two-phase Lamport call; with --sweep
-the tp=8 sweep (M = 256..8192, N=7168, K=2048) in the bf16 forms.
+`secondary` holds every other workload, each timed launch by launch with HIP
+events on the kernel's stream (median, min and p90 over --iters launches) and
+carrying a `roofline` object (algorithmic work per launch over the median
+launch time, against the MFMA or HBM peak) and, where the oracle has one, a
+bounded `cpu_baseline`:
+  gemm_rs_tiny          R=2, X[256,256], W[256,512] (launch-bound)
+  gemm_rs_tp4_prestaged the headline's kernel with every partial landed
+  gemm_rs_tp8_m{M}      R=8, X[M,2048], W[2048,7168], M = 256, 1024, 4096, 8192
+  lamport_ar_rmsnorm    8 x [4096,7168] partials, RMSNorm over 7168
+  combine_reduce        [4096,8,7168] top-8 weighted sum, register pipeline and
+                        the LDS-staged pipeline
+  lamport_2phase        rank 0 of 8 of the two-phase call at [4096,7168]
+  gemm_rs_fp8_tp4       fp8 e4m3fn block-scaled GEMM-RS on the tp=4 share
+  gemm_rs_ring_tp4      one push-ring hop: step with the producer, and pre-staged
 
 `cpu_baseline` times the CPU oracle (oracle/, test infrastructure) on a
 bounded row sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--iters I] [--sweep]
+                       [--no-cpu] [--only LEG]
 """
 from __future__ import annotations
 
@@ -34,15 +42,21 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 
-LAMPORT_BYTES = 998_258_688 + 7168 * 2   # read 8P + write P + re-arm 8P (+ gamma)
-LAMPORT_BYTES_NO_REARM = 528_482_304 + 7168 * 2
-COMBINE_BYTES = 528_613_376              # read x + gate + write out
+P_4096x7168 = 4096 * 7168 * 2                 # one [4096,7168] bf16 buffer
+LAMPORT_BYTES = 17 * P_4096x7168 + 7168 * 2   # read 8P + write P + re-arm 8P (+ gamma)
+LAMPORT_BYTES_NO_REARM = 9 * P_4096x7168 + 7168 * 2
+COMBINE_BYTES = 8 * P_4096x7168 + 4096 * 8 * 4 + P_4096x7168   # read x + gate + write out
+# two-phase Lamport, one rank's call at [4096,7168]: phase A reads P and stores
+# P (its part into 8 stagings), phase B reads P, re-arms P, writes out P (+gamma)
+LAMPORT2_BYTES = 5 * P_4096x7168 + 7168 * 2
 # The emulated peers publish their tiles' ready bits eight tiles per release.
 # On one GPU an agent-scope release writes back the L2 of the XCD it runs on --
 # the L2 the GEMM is using -- which a remote peer's release never does to this
-# GPU; one release per tile costs the step ~17 us of that artifact.  The step
-# with one release per tile is reported beside the headline.
+# GPU.  The step with one release per tile is reported beside the headline.
 PRODUCER_TILES_PER_RELEASE = 8
+
+LEGS = ("gemm_rs", "gemm_rs_tiny", "gemm_rs_prestaged", "gemm_rs_tp8", "lamport", "combine", "combine_lds",
+        "lamport_2phase", "gemm_rs_fp8", "gemm_rs_ring", "gemm_rs_ring_prestaged")
 
 _side_stream = None
 
@@ -54,9 +68,6 @@ def side_stream(torch):
     if _side_stream is None:
         _side_stream = torch.cuda.Stream()
     return _side_stream
-# two-phase Lamport, one rank's call at [4096,7168]: phase A reads P and stores
-# P (its part into 8 stagings), phase B reads P, re-arms P, writes out P (+gamma)
-LAMPORT2_BYTES = 5 * 58_720_256 + 7168 * 2
 
 
 class _HipEvents:
@@ -78,7 +89,7 @@ class _HipEvents:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
 
-    def create(self, flags):
+    def create(self, flags=DISABLE_SYSTEM_FENCE):
         e = self.ct.c_void_p()
         if self.lib.hipEventCreateWithFlags(self.ct.byref(e), flags) != 0:
             raise RuntimeError("hipEventCreateWithFlags failed")
@@ -103,19 +114,73 @@ class _HipEvents:
             self.lib.hipEventDestroy(e)
 
 
+def stats(ms):
+    """Median, min, p90 and mean of per-launch times (ms)."""
+    s = sorted(ms)
+    n = len(s)
+    return dict(ms_median=s[n // 2], ms_min=s[0], ms_p90=s[min(n - 1, (9 * n) // 10)], ms_mean=sum(s) / n, iters=n)
+
+
+def time_launches(torch, call, iters, warmup, before=None):
+    """Times `call()` launch by launch with fence-free HIP events on the
+    current stream; `before()` (untimed) runs ahead of every launch."""
+    H = _HipEvents()
+    main = torch.cuda.current_stream()
+    n = iters + warmup
+    es = [H.create() for _ in range(n)]
+    ee = [H.create() for _ in range(n)]
+    for i in range(n):
+        if before is not None:
+            before()
+        H.record(es[i], main)
+        call()
+        H.record(ee[i], main)
+    torch.cuda.synchronize()
+    ms = [H.elapsed_ms(es[i], ee[i]) for i in range(warmup, n)]
+    H.destroy(es + ee)
+    return stats(ms)
+
+
+def roofline(bound, work, st, peak, unit, traffic=None, kernel=None):
+    """Roofline object: algorithmic work per launch over the median launch
+    time (FLOP -> TFLOP/s, bytes -> GB/s), against `peak`."""
+    t = st["ms_median"] * 1e-3
+    achieved = work / t / (1e12 if unit == "TFLOP/s" else 1e9)
+    r = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+         "traffic": traffic}
+    if kernel:
+        r["kernel"] = kernel
+    return r
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=50, help="timed steps of the headline")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sweep", action="store_true", help="also time the tp=8 sweep and the pre-staged tp=4 kernel")
-    ap.add_argument("--only", default=None, choices=[None, "gemm_rs", "gemm_rs_prestaged", "gemm_rs_ring",
-                                                   "gemm_rs_ring_prestaged", "gemm_rs_fp8", "lamport", "lamport_2phase",
-                                                   "combine"],
-                    help="run a single path (used for per-kernel profiles; counter collection serializes "
+    ap.add_argument("--iters", type=int, default=100, help="timed launches of every other workload")
+    ap.add_argument("--sweep", action="store_true", help="also time the push-ring hop over the tp=8 sweep")
+    ap.add_argument("--only", default=None, choices=[None, *LEGS],
+                    help="run a single leg (used for per-kernel profiles; counter collection serializes "
                          "kernels, so the GEMM's counters are taken pre-staged, without the producer stream)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--m", type=int, default=None, help="with --only gemm_rs_tp8: one M of the sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baselines")
     return ap.parse_args()
+
+
+def _up(torch, a):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(a).view("int16")).view(torch.bfloat16).to(torch.device("cuda:0"))
+
+
+def _ready_all(torch, R, absent, words, tiles):
+    import numpy as np
+    full = np.zeros((R, words), np.uint32)
+    for p in range(R):
+        if p != absent:
+            for t in range(tiles):
+                full[p, t // 32] |= np.uint32(1 << (t % 32))
+    return torch.from_numpy(full.view(np.int32)).to(torch.device("cuda:0"))
 
 
 def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs=0, per_release=1):
@@ -127,8 +192,7 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
     zero again when it ends and needs no clearing kernel.  The producer of step
     i, on the side stream, waits for GEMM i-1 to end (it reuses recv and
     ready_in) and then runs while GEMM i does; GEMM i's owner tiles wait for
-    its bits.  ready_out is only ever OR-ed into.  The producer's waves share
-    CUs with the GEMM's (the chosen tile leaves registers for them).
+    its bits.  ready_out is only ever OR-ed into.
 
     Returns the wall time per step and the GEMM's average launch duration from
     HIP events recorded on its stream just before and after each launch.
@@ -144,12 +208,8 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
     # the one this rank starts (ring)
     absent = (owner + R - 1) % R if ring else owner
     parts = case["up"] if ring else case["recv"]
-
-    def up(a):
-        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
-
-    x, w = up(case["x"]), up(case["w"])
-    src = [None if p == absent else up(parts[p]) for p in range(R)]
+    x, w = _up(torch, case["x"]), _up(torch, case["w"])
+    src = [None if p == absent else _up(torch, parts[p]) for p in range(R)]
     recv = [None if p == absent else torch.zeros_like(src[p]) for p in range(R)]
     words = A.gemm_rs_flag_words(M, N, R)
     tiles = ((seg + 127) // 128) * ((N + 127) // 128)
@@ -161,11 +221,11 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     main = torch.cuda.current_stream()
     side = side_stream(torch)
-    tile = A.gemm_rs_pick_tile(M, N, K, R, owner, publish=True)
+    tile = (A.gemm_rs_ring_pick_tile if ring else A.gemm_rs_pick_tile)(M, N, K, R, owner, publish=True)
     n_ev = steps + warmup
     H = _HipEvents()
-    ev_gs = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n_ev)]
-    ev_ge = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n_ev)]
+    ev_gs = [H.create() for _ in range(n_ev)]
+    ev_ge = [H.create() for _ in range(n_ev)]
 
     def step(i):
         if i > 0:
@@ -189,17 +249,22 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
         step(i)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    gemm_ms = sum(H.elapsed_ms(ev_gs[i], ev_ge[i]) for i in range(warmup, warmup + steps)) / steps
+    gemm = stats([H.elapsed_ms(ev_gs[i], ev_ge[i]) for i in range(warmup, warmup + steps)])
     H.destroy(ev_gs + ev_ge)
     if int(status.item()) != 0:
         raise RuntimeError("a readiness wait timed out during the benchmark")
     flops = 2.0 * M * N * K
-    return dict(ms_per_step=wall * 1e3, tflops=flops / wall / 1e12, gemm_ms=gemm_ms,
-                gemm_tflops=flops / (gemm_ms * 1e-3) / 1e12, tile=A.TILE_NAMES[tile], flops=flops,
-                M=M, N=N, K=K, R=R)
+    return dict(ms_per_step=wall * 1e3, tflops=flops / wall / 1e12, gemm=gemm, tile=A.TILE_NAMES[tile],
+                flops=flops, M=M, N=N, K=K, R=R)
 
 
-def gemm_rs_prestaged(A, inputs, torch, steps, warmup, num, M=None, ring=False):
+def gemm_rs_bytes(M, N, K, R):
+    """Algorithmic bytes of one GEMM-RS call: X + W + (R-1) partials + out + send."""
+    seg = M // R
+    return 2.0 * (M * K + K * N + (R - 1) * seg * N + seg * N + (M - seg) * N)
+
+
+def gemm_rs_prestaged(A, inputs, torch, iters, warmup, num, M=None, ring=False, counters=None):
     """GEMM + reduce-scatter epilogue with every partial landed beforehand (all
     ready bits set): the kernel alone.  ring=True times the push-ring hop."""
     dev = torch.device("cuda:0")
@@ -214,26 +279,15 @@ def gemm_rs_prestaged(A, inputs, torch, steps, warmup, num, M=None, ring=False):
     seg = M // R
     absent = (owner + R - 1) % R if ring else owner
     parts = case["up"] if ring else case["recv"]
-
-    def up(a):
-        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
-
-    x, w = up(case["x"]), up(case["w"])
-    recv = [None if p == absent else up(parts[p]) for p in range(R)]
+    x, w = _up(torch, case["x"]), _up(torch, case["w"])
+    recv = [None if p == absent else _up(torch, parts[p]) for p in range(R)]
     words = A.gemm_rs_flag_words(M, N, R)
     tiles = ((seg + 127) // 128) * ((N + 127) // 128)
-    import numpy as np
-    full = np.zeros((R, words), np.uint32)
-    for p in range(R):
-        if p != absent:
-            for t in range(tiles):
-                full[p, t // 32] |= np.uint32(1 << (t % 32))
-    rin = torch.from_numpy(full.view(np.int32)).to(dev)
+    rin = _ready_all(torch, R, absent, words, tiles)
     rout = torch.zeros((R, words), dtype=torch.int32, device=dev)
     out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
     send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    tile = A.gemm_rs_pick_tile(M, N, K, R, owner, publish=True)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tile = (A.gemm_rs_ring_pick_tile if ring else A.gemm_rs_pick_tile)(M, N, K, R, owner, publish=True)
 
     def call():
         if ring:
@@ -241,57 +295,52 @@ def gemm_rs_prestaged(A, inputs, torch, steps, warmup, num, M=None, ring=False):
         else:
             A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(steps):
-        call()
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / steps
+    st = time_launches(torch, call, iters, warmup)
     flops = 2.0 * M * N * K
-    byts = 2.0 * (M * K + K * N + (R - 1) * seg * N + seg * N + (M - seg) * N)
-    return dict(M=M, N=N, K=K, R=R, tile=A.TILE_NAMES[tile], ms=ms, tflops=flops / ms / 1e9,
-                frac_mfma=flops / ms / 1e9 / PEAK_BF16_TFLOPS, gbs=byts / ms / 1e6,
-                frac_hbm=byts / ms / 1e6 / PEAK_HBM_GBS)
+    byts = gemm_rs_bytes(M, N, K, R)
+    t = st["ms_median"] * 1e-3
+    # HBM-bound where the arithmetic intensity is below the ridge point
+    hbm = flops / byts < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
+    traffic = measured_traffic(counters, A.TILE_NAMES[tile]) if counters else None
+    rf = (roofline("hbm", byts, st, PEAK_HBM_GBS, "GB/s", traffic, "gemm_rs_ring_kernel" if ring else "gemm_rs_kernel")
+          if hbm else
+          roofline("mfma", flops, st, PEAK_BF16_TFLOPS, "TFLOP/s", traffic,
+                   "gemm_rs_ring_kernel" if ring else "gemm_rs_kernel"))
+    return dict(M=M, N=N, K=K, R=R, tile=A.TILE_NAMES[tile], **st, tflops=flops / t / 1e12,
+                frac_mfma=flops / t / 1e12 / PEAK_BF16_TFLOPS, gbs=byts / t / 1e9,
+                frac_hbm=byts / t / 1e9 / PEAK_HBM_GBS, roofline=rf)
 
 
-def lamport(A, inputs, torch, steps, warmup):
+def lamport(A, inputs, torch, iters, warmup, case):
     dev = torch.device("cuda:0")
-    case = inputs.lamport_case()
     S, M, N = case["S"], case["M"], case["N"]
-    src = torch.from_numpy(case["src"].view("int16")).view(torch.bfloat16).to(dev)
-    gamma = torch.from_numpy(case["gamma"].view("int16")).view(torch.bfloat16).to(dev)
+    src = _up(torch, case["src"])
+    gamma = _up(torch, case["gamma"])
     order = torch.from_numpy(case["order"]).to(dev)
-    st = torch.empty((S, M, N), dtype=torch.bfloat16, device=dev)
+    st_buf = torch.empty((S, M, N), dtype=torch.bfloat16, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    A.lamport_prefill(st)   # arming: once, before any timing
+    A.lamport_prefill(st_buf)   # arming: once, before any timing
     main = torch.cuda.current_stream()
     side = side_stream(torch)
-    n = steps + warmup
-    # fence-free HIP events on the consumer's stream, as for the GEMM
-    H = _HipEvents()
-    es = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n)]
-    ee = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n)]
-    for i in range(n):
-        side.wait_stream(main)   # publish only into re-armed staging
-        A.lamport_publish(src, st, order, stream=side)
+
+    def publish():   # the emulated peers land their partials into the re-armed staging (untimed)
+        side.wait_stream(main)
+        A.lamport_publish(src, st_buf, order, stream=side)
         main.wait_stream(side)
-        H.record(es[i], main)
-        A.ar_rmsnorm_lamport(st, gamma, out, case["eps"], status=status, stream=main)
-        H.record(ee[i], main)
-    torch.cuda.synchronize()
+
+    st = time_launches(torch, lambda: A.ar_rmsnorm_lamport(st_buf, gamma, out, case["eps"], status=status),
+                       iters, warmup, before=publish)
     if int(status.item()) != 0:
         raise RuntimeError("Lamport consumer timed out")
-    ms = sum(H.elapsed_ms(es[i], ee[i]) for i in range(warmup, n)) / steps
-    H.destroy(es + ee)
-    return dict(ms=ms, gbs=LAMPORT_BYTES / ms / 1e6, frac_hbm=LAMPORT_BYTES / ms / 1e6 / PEAK_HBM_GBS,
-                gbs_no_rearm_bytes=LAMPORT_BYTES_NO_REARM / ms / 1e6, S=S, M=M, N=N)
+    t = st["ms_median"] * 1e-3
+    return dict(**st, gbs=LAMPORT_BYTES / t / 1e9, frac_hbm=LAMPORT_BYTES / t / 1e9 / PEAK_HBM_GBS,
+                gbs_no_rearm_bytes=LAMPORT_BYTES_NO_REARM / t / 1e9, S=S, M=M, N=N,
+                roofline=roofline("hbm", LAMPORT_BYTES, st, PEAK_HBM_GBS, "GB/s",
+                                  measured_traffic("lamport", "512x2"), "ar_rmsnorm_kernel"))
 
 
-def gemm_rs_fp8_prestaged(A, inputs, torch, steps, warmup):
+def gemm_rs_fp8_prestaged(A, inputs, torch, iters, warmup):
     """fp8 e4m3fn block-scaled GEMM + reduce-scatter epilogue on the tp=4 share
     (X [4096,2048], W^T [4096,2048], 1x128 / 128x128 fp32 scales, R=4), peer
     partials landed beforehand: the kernel alone."""
@@ -302,51 +351,33 @@ def gemm_rs_fp8_prestaged(A, inputs, torch, steps, warmup):
     seg = M // R
     u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     x, wt, xs, ws = u8(case["x"]), u8(case["wt"]), u8(case["xs"]), u8(case["ws"])
-    recv = [None if q == owner else torch.from_numpy(case["recv"][q].view("int16")).view(torch.bfloat16).to(dev)
-            for q in range(R)]
+    recv = [None if q == owner else _up(torch, case["recv"][q]) for q in range(R)]
     words = A.gemm_rs_flag_words(M, N, R)
-    tiles = ((seg + 127) // 128) * ((N + 127) // 128)
-    full = np.zeros((R, words), np.uint32)
-    for q in range(R):
-        if q != owner:
-            for t in range(tiles):
-                full[q, t // 32] |= np.uint32(1 << (t % 32))
-    rin = torch.from_numpy(full.view(np.int32)).to(dev)
+    rin = _ready_all(torch, R, owner, words, ((seg + 127) // 128) * ((N + 127) // 128))
     rout = torch.zeros((R, words), dtype=torch.int32, device=dev)
     out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
     send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-
-    def call():
-        A.gemm_rs_fp8(x, xs, wt, ws, recv, rin, out, R, owner, send=send, ready_out=rout)
-
-    for _ in range(warmup):
-        call()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(steps):
-        call()
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / steps
+    st = time_launches(torch, lambda: A.gemm_rs_fp8(x, xs, wt, ws, recv, rin, out, R, owner, send=send,
+                                                    ready_out=rout), iters, warmup)
     flops = 2.0 * M * N * K
     byts = M * K + N * K + 4.0 * (M + N // 128) * (K // 128) + 2.0 * ((R - 1) * seg * N + seg * N + (M - seg) * N)
-    return dict(M=M, N=N, K=K, R=R, tile="256x256", ms=ms, tflops=flops / ms / 1e9,
-                frac_mfma_fp8=flops / ms / 1e9 / PEAK_FP8_TFLOPS, gbs=byts / ms / 1e6,
-                frac_hbm=byts / ms / 1e6 / PEAK_HBM_GBS)
+    t = st["ms_median"] * 1e-3
+    return dict(M=M, N=N, K=K, R=R, tile="256x256", **st, tflops=flops / t / 1e12,
+                frac_mfma_fp8=flops / t / 1e12 / PEAK_FP8_TFLOPS, gbs=byts / t / 1e9,
+                frac_hbm=byts / t / 1e9 / PEAK_HBM_GBS,
+                roofline=roofline("mfma", flops, st, PEAK_FP8_TFLOPS, "TFLOP/s", None, "gemm_rs_kernel (fp8)"))
 
 
-def lamport_2phase(A, inputs, torch, steps, warmup):
+def lamport_2phase(A, inputs, torch, iters, warmup, case):
     """Two-phase Lamport AR + RMSNorm on rank 0 of 8, [4096,7168]: the seven
     peers' phase A is emulated on a side stream after the previous call has
     re-armed (their stores then wait in rank 0's staging); only the call itself
     is timed: phase A of its own part (read P, store P across the 8 stagings)
     and phase B (read P, re-arm P, write out P)."""
     dev = torch.device("cuda:0")
-    case = inputs.lamport_case()
     R, M, N = case["S"], case["M"], case["N"]
-    ins = [torch.from_numpy(case["src"][r].view("int16")).view(torch.bfloat16).to(dev) for r in range(R)]
-    gamma = torch.from_numpy(case["gamma"].view("int16")).view(torch.bfloat16).to(dev)
+    ins = [_up(torch, case["src"][r]) for r in range(R)]
+    gamma = _up(torch, case["gamma"])
     stg = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
     for t in stg:
         A.lamport_prefill(t)
@@ -354,56 +385,50 @@ def lamport_2phase(A, inputs, torch, steps, warmup):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     main = torch.cuda.current_stream()
     side = side_stream(torch)
-    n = steps + warmup
-    # fence-free HIP events on the consumer's stream, as for the GEMM
-    H = _HipEvents()
-    es = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n)]
-    ee = [H.create(H.DISABLE_SYSTEM_FENCE) for _ in range(n)]
-    for i in range(n):
+
+    def peers():
         side.wait_stream(main)
         for d in range(1, R):
             A.emu_lamport_phase_a(ins, stg, d, stream=side)
         main.wait_stream(side)
-        H.record(es[i], main)
-        A.ar_rmsnorm_lamport_2phase(ins, stg, gamma, out, 0, case["eps"], status=status, stream=main)
-        H.record(ee[i], main)
-    torch.cuda.synchronize()
+
+    st = time_launches(torch, lambda: A.ar_rmsnorm_lamport_2phase(ins, stg, gamma, out, 0, case["eps"],
+                                                                  status=status), iters, warmup, before=peers)
     if int(status.item()) != 0:
         raise RuntimeError("two-phase Lamport call timed out")
-    ms = sum(H.elapsed_ms(es[i], ee[i]) for i in range(warmup, n)) / steps
-    H.destroy(es + ee)
-    return dict(ms=ms, gbs=LAMPORT2_BYTES / ms / 1e6, frac_hbm=LAMPORT2_BYTES / ms / 1e6 / PEAK_HBM_GBS,
-                R=R, M=M, N=N)
+    t = st["ms_median"] * 1e-3
+    return dict(**st, gbs=LAMPORT2_BYTES / t / 1e9, frac_hbm=LAMPORT2_BYTES / t / 1e9 / PEAK_HBM_GBS,
+                R=R, M=M, N=N, roofline=roofline("hbm", LAMPORT2_BYTES, st, PEAK_HBM_GBS, "GB/s",
+                                                 None, "lamport2_kernel"))
 
 
-def combine(A, inputs, torch, steps, warmup):
+def combine(A, inputs, torch, iters, warmup, case, pipeline="registers"):
     dev = torch.device("cuda:0")
-    case = inputs.combine_case()
-    x = torch.from_numpy(case["x"].view("int16")).view(torch.bfloat16).to(dev)
+    x = _up(torch, case["x"])
     gate = torch.from_numpy(case["gate"]).to(dev)
     out = torch.empty((case["T"], case["H"]), dtype=torch.bfloat16, device=dev)
-    for _ in range(warmup):
-        A.combine_reduce(x, gate, out)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(steps):
-        A.combine_reduce(x, gate, out)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / steps
-    return dict(ms=ms, gbs=COMBINE_BYTES / ms / 1e6, frac_hbm=COMBINE_BYTES / ms / 1e6 / PEAK_HBM_GBS,
-                T=case["T"], E=case["E"], H=case["H"])
+    st = time_launches(torch, lambda: A.combine_reduce(x, gate, out, pipeline=pipeline), iters, warmup)
+    t = st["ms_median"] * 1e-3
+    key = "combine" if pipeline == "registers" else "combine_lds"
+    return dict(**st, gbs=COMBINE_BYTES / t / 1e9, frac_hbm=COMBINE_BYTES / t / 1e9 / PEAK_HBM_GBS,
+                T=case["T"], E=case["E"], H=case["H"], pipeline=pipeline,
+                roofline=roofline("hbm", COMBINE_BYTES, st, PEAK_HBM_GBS, "GB/s",
+                                  measured_traffic(key, pipeline),
+                                  "combine_regs_kernel" if pipeline == "registers" else "combine_kernel"))
 
 
-def cpu_baseline(inputs, budget_s=10.0):
-    """The CPU oracle (oracle/, test infrastructure) on the headline workload.
+# ---- CPU baselines: the oracle (test infrastructure) on bounded samples --------
 
-    Row bands of the tp=4 GEMM-RS share are run back to back, wrapping around
-    the 4096 rows, until about `budget_s` seconds of wall time on all host
-    threads have been spent; the rate is FLOPs of the rows done / time."""
+def _cpu_note(what, done, total, unit_name, secs):
+    return "%s: %d of %d %s, %.1f s wall, %s" % (what, done, total, unit_name, secs,
+                                                   platform.processor() or platform.machine())
+
+
+def cpu_baseline_gemm_rs(inputs, case, budget_s, what):
+    """Row bands of a GEMM-RS case run back to back (wrapping around its M
+    rows) until about `budget_s` of wall time; rate = FLOPs of the rows done /
+    time (TFLOP/s)."""
     import oracle
-    case = inputs.workload_gemm_rs(2)
     M, N, K, R = case["M"], case["N"], case["K"], case["R"]
     oracle.gemm_rs(case["x"], case["w"], case["recv"], R, case["owner"], rows=(0, 16))   # load + warm
     rows, t_used, r0, band = 0, 0.0, 0, 64
@@ -419,35 +444,66 @@ def cpu_baseline(inputs, budget_s=10.0):
         r0 = 0 if r1 == M else r1
     flops = 2.0 * rows * N * K
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d rows (%.2f passes over the %d rows) of the tp=4 GEMM-RS share, %.1f s wall, %s" % (
-                rows, rows / M, M, t_used, platform.processor() or platform.machine())}
+            "sample": _cpu_note(what, rows, M, "rows (%.2f passes)" % (rows / M), t_used)}
 
 
-COUNTERS_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "gemm_rs_tp4_counters.txt")
-# the kernel body and the direct-form entry (the counters go stale when either changes)
-KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "all_reduce_epilogues_amd", "csrc", f)
-                  for f in ("gemm_rs_impl.h", "gemm_rs.hip")]
+def cpu_baseline_rows(fn, total, per_unit_bytes, budget_s, what, unit_name):
+    """`fn((r0, r1))` over row/token bands until about `budget_s`; rate =
+    algorithmic bytes of the units done / time (GB/s)."""
+    import oracle
+    fn((0, 1))
+    done, t_used, r0, band = 0, 0.0, 0, 8
+    while t_used < budget_s:
+        r1 = min(total, r0 + band)
+        t = time.perf_counter()
+        fn((r0, r1))
+        dt = time.perf_counter() - t
+        t_used += dt
+        done += r1 - r0
+        band = max(1, min(total, int((r1 - r0) * 0.5 / max(dt, 1e-3))))
+        r0 = 0 if r1 == total else r1
+    return {"value": done * per_unit_bytes / t_used / 1e9, "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": _cpu_note(what, done, total, unit_name, t_used)}
 
 
-def kernel_source_digest():
+# ---- stored HBM-traffic counters -------------------------------------------------
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "all_reduce_epilogues_amd", "csrc")
+# counter record per workload: file under profiles/ and the kernel sources it was
+# measured on (the record goes stale when one of them changes)
+COUNTERS = {
+    "gemm_rs_tp4": ("gemm_rs_tp4_counters.txt", ("gemm_rs_impl.h", "gemm_rs.hip")),
+    "gemm_rs_tp8_m256": ("gemm_rs_tp8_m256_counters.txt", ("gemm_rs_impl.h", "gemm_rs.hip")),
+    "gemm_rs_tp8_m8192": ("gemm_rs_tp8_m8192_counters.txt", ("gemm_rs_impl.h", "gemm_rs.hip")),
+    "lamport": ("lamport_counters.txt", ("lamport.hip",)),
+    "combine": ("combine_counters.txt", ("combine.hip",)),
+    "combine_lds": ("combine_counters_lds.txt", ("combine.hip",)),
+}
+COUNTERS_FILE = None   # (tests) one record file used for every key instead
+
+
+def kernel_source_digest(key="gemm_rs_tp4"):
     import hashlib
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+    for f in COUNTERS[key][1]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(tile):
-    """HBM-side bytes per launch of the GEMM kernel from the stored rocprofv3
-    FETCH_SIZE / WRITE_SIZE passes (scaled by the copy-kernel calibration), or
-    None when the kernel source or the tile has changed since they were taken."""
+def measured_traffic(key, tile):
+    """HBM-side bytes per launch from the stored rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (scaled by the copy-kernel calibration), or None when
+    there is no record, or the kernel sources or the launch shape (`tile`)
+    have changed since it was taken."""
+    path = COUNTERS_FILE or os.path.join(HERE, "profiles", COUNTERS[key][0])
     try:
-        with open(COUNTERS_FILE) as f:
+        with open(path) as f:
             rec = dict(line.split(": ", 1) for line in f.read().splitlines()
                        if line and not line.startswith("#") and ": " in line)
-        digest = kernel_source_digest()
-    except OSError:
+        digest = kernel_source_digest(key)
+    except (OSError, KeyError):
         return None
     if rec.get("source_sha256", "").strip() != digest or rec.get("tile", "").strip() != tile:
         return None
@@ -466,37 +522,72 @@ def main():
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs the MI355X GPU")
     A.lib()
+    run = lambda leg: a.only in (None, leg)
     secondary = {}
-    head = None
-    if a.only in (None, "gemm_rs"):
+    head = r1 = None
+    it, wu = a.iters, min(10, a.warmup if a.only else 10)
+    if run("gemm_rs"):
         head = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, per_release=PRODUCER_TILES_PER_RELEASE)
         r1 = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, per_release=1)
-        secondary["gemm_rs_tp4_step_one_release_per_tile"] = dict(
-            ms_per_step=r1["ms_per_step"], tflops=r1["tflops"], kernel_ms=r1["gemm_ms"],
-            frac_mfma=r1["gemm_tflops"] / PEAK_BF16_TFLOPS)
-    if a.only in (None, "gemm_rs_ring"):
+    if run("gemm_rs_tiny"):
+        secondary["gemm_rs_tiny"] = gemm_rs_prestaged(A, inputs, torch, it, wu, 1)
+    if run("gemm_rs_prestaged") or run("gemm_rs"):
+        secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, it, wu, 2, counters="gemm_rs_tp4")
+    if run("gemm_rs_tp8"):
+        for m in ([a.m] if a.m else inputs.TP8_M_SWEEP):
+            key = "gemm_rs_tp8_m%d" % m
+            secondary[key] = gemm_rs_prestaged(A, inputs, torch, it, wu, 3, M=m,
+                                               counters=key if key in COUNTERS else None)
+    lam_case = None
+    if run("lamport") or run("lamport_2phase"):
+        lam_case = inputs.lamport_case()
+    if run("lamport"):
+        secondary["lamport_ar_rmsnorm"] = lamport(A, inputs, torch, it, wu, lam_case)
+    comb_case = None
+    if run("combine") or run("combine_lds"):
+        comb_case = inputs.combine_case()
+    if run("combine"):
+        secondary["combine_reduce"] = combine(A, inputs, torch, it, wu, comb_case)
+    if run("combine_lds"):
+        secondary["combine_reduce_lds"] = combine(A, inputs, torch, it, wu, comb_case, pipeline="lds")
+    if run("lamport_2phase"):
+        secondary["lamport_2phase_ar_rmsnorm"] = lamport_2phase(A, inputs, torch, it, wu, lam_case)
+    if run("gemm_rs_fp8"):
+        secondary["gemm_rs_fp8_tp4_prestaged"] = gemm_rs_fp8_prestaged(A, inputs, torch, it, wu)
+    if run("gemm_rs_ring"):
         r = gemm_rs_concurrent(A, inputs, torch, a.steps, a.warmup, ring=True, per_release=PRODUCER_TILES_PER_RELEASE)
         secondary["gemm_rs_ring_tp4_step"] = dict(ms_per_step=r["ms_per_step"], tflops=r["tflops"],
-                                                  kernel_ms=r["gemm_ms"], kernel_tflops=r["gemm_tflops"],
-                                                  frac_mfma=r["gemm_tflops"] / PEAK_BF16_TFLOPS, tile=r["tile"])
-    if a.only in (None, "lamport"):
-        secondary["lamport_ar_rmsnorm"] = lamport(A, inputs, torch, max(10, a.steps // 2), 3)
-    if a.only in (None, "combine"):
-        secondary["combine_reduce"] = combine(A, inputs, torch, max(10, a.steps // 2), 3)
-    if a.only in (None, "lamport_2phase"):
-        secondary["lamport_2phase_ar_rmsnorm"] = lamport_2phase(A, inputs, torch, max(10, a.steps // 2), 3)
-    if a.only in (None, "gemm_rs", "gemm_rs_prestaged"):
-        secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2)
-    if a.only in (None, "gemm_rs_fp8"):
-        secondary["gemm_rs_fp8_tp4_prestaged"] = gemm_rs_fp8_prestaged(A, inputs, torch, a.steps, a.warmup)
-    if a.only in (None, "gemm_rs_ring", "gemm_rs_ring_prestaged"):
-        secondary["gemm_rs_ring_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 2,
-                                                                    ring=True)
+                                                  kernel=r["gemm"], tile=r["tile"])
+    if run("gemm_rs_ring") or run("gemm_rs_ring_prestaged"):
+        secondary["gemm_rs_ring_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, it, wu, 2, ring=True)
     if a.sweep:
-        secondary["gemm_rs_tp8_sweep"] = [gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 3, M=m)
-                                         for m in inputs.TP8_M_SWEEP]
-        secondary["gemm_rs_ring_tp8_sweep"] = [gemm_rs_prestaged(A, inputs, torch, a.steps, a.warmup, 3, M=m,
-                                                                 ring=True) for m in inputs.TP8_M_SWEEP]
+        secondary["gemm_rs_ring_tp8_sweep"] = [gemm_rs_prestaged(A, inputs, torch, it, wu, 3, M=m, ring=True)
+                                               for m in inputs.TP8_M_SWEEP]
+
+    # CPU baselines (oracle, bounded samples of each workload; reported, never a target)
+    cpu = None
+    if not a.no_cpu:
+        import oracle
+        if head:
+            cpu = cpu_baseline_gemm_rs(inputs, inputs.workload_gemm_rs(2), 10.0, "tp=4 GEMM-RS share")
+        if "gemm_rs_tp8_m8192" in secondary:
+            c8 = inputs.workload_gemm_rs(3, M=8192)
+            base = cpu_baseline_gemm_rs(inputs, c8, 4.0, "tp=8 GEMM-RS, M=8192")
+            for m in inputs.TP8_M_SWEEP:   # the oracle's rate does not depend on M; one sample serves the sweep
+                if "gemm_rs_tp8_m%d" % m in secondary:
+                    secondary["gemm_rs_tp8_m%d" % m]["cpu_baseline"] = base
+        if lam_case is not None and "lamport_ar_rmsnorm" in secondary:
+            c = lam_case
+            secondary["lamport_ar_rmsnorm"]["cpu_baseline"] = cpu_baseline_rows(
+                lambda rows: oracle.ar_rmsnorm(c["src"], c["gamma"], c["eps"], rows=rows), c["M"],
+                LAMPORT_BYTES / c["M"], 4.0, "Lamport AR+RMSNorm, 8 x [4096,7168] (algorithmic bytes per row)",
+                "rows")
+        if comb_case is not None and "combine_reduce" in secondary:
+            c = comb_case
+            secondary["combine_reduce"]["cpu_baseline"] = cpu_baseline_rows(
+                lambda tok: oracle.combine(c["x"], c["gate"], tokens=tok), c["T"], COMBINE_BYTES / c["T"], 4.0,
+                "combine, [4096,8,7168] (algorithmic bytes per token)", "tokens")
+
     line = {
         "metric": "GEMM-RS TFLOP/s + % bf16 MFMA peak; combine/RMSNorm GB/s + % HBM peak",
         "value": head["tflops"] if head else None,
@@ -519,13 +610,17 @@ def main():
                    "tile": head["tile"] if head else None},
     }
     if head:
-        achieved = head["flops"] / (head["gemm_ms"] * 1e-3) / 1e12
-        line["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                            "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(head["tile"]),
-                            "kernel": "gemm_rs_kernel", "avg_kernel_ms": head["gemm_ms"]}
+        line["config"]["one_release_per_tile"] = {
+            "tflops": r1["tflops"], "ms_per_step": r1["ms_per_step"], "kernel_ms_median": r1["gemm"]["ms_median"],
+            "note": "the same step with the producer releasing after every tile"}
+        g = head["gemm"]
+        line["roofline"] = roofline("mfma", head["flops"], g, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                    measured_traffic("gemm_rs_tp4", head["tile"]), "gemm_rs_kernel")
+        line["roofline"].update(kernel_ms_median=g["ms_median"], kernel_ms_min=g["ms_min"],
+                                kernel_ms_p90=g["ms_p90"])
     line["secondary"] = secondary
-    if not a.no_cpu and head:
-        line["cpu_baseline"] = cpu_baseline(inputs)
+    if cpu:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
