@@ -173,15 +173,17 @@ __host__ __device__ __forceinline__ void chunks_of_block(const GemmRsParams &p, 
 }
 
 __host__ __device__ __forceinline__ void tile_of_block(const GemmRsParams &p, int b, int &rb, int &cb) {
-    // XCD-aware remap inside full rounds of 8*C blocks: consecutive schedule
-    // entries land on the same XCD (blocks are dealt to XCDs round-robin).
+    // XCD-aware remap inside rounds of 8*C blocks: consecutive schedule
+    // entries land on the same XCD (blocks are dealt to XCDs round-robin), so
+    // the blocks one XCD runs share X rows and W columns in its L2.  A last,
+    // partial round of 8*C' blocks is remapped the same way with C' in place
+    // of C (left in order when its size is not a multiple of 8).
     const int C = p.xcd_chunk;
     const int round = kXcds * C;
     int s = b;
-    if ((b / round + 1) * round <= p.nWG) {
-        const int r = b / round, j = b % round;
-        s = r * round + (j % kXcds) * C + j / kXcds;
-    }
+    const int r = b / round, j = b % round;
+    const int in_round = min(round, p.nWG - r * round);  // blocks of b's round
+    if (in_round % kXcds == 0) s = r * round + (j % kXcds) * (in_round / kXcds) + j / kXcds;
     // G row blocks at a time, column-major inside the group.
     const int per_group = p.group * p.nCB;
     const int g = s / per_group, within = s % per_group;
