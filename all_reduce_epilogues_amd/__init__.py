@@ -8,7 +8,8 @@ raises if ``libarepi.so`` is missing or a kernel launch is refused.
 
 Names mirror the C entry points without the ``arepi_`` prefix:
   gemm_rs_fused, gemm_rs_supports, gemm_rs_flag_words, gemm_rs_pick_tile, gemm_rs_schedule,
-  lamport_prefill, lamport_publish, ar_rmsnorm_lamport, combine_reduce (and its
+  lamport_prefill, lamport_publish, ar_rmsnorm_lamport, ar_rmsnorm_lamport_noalloc,
+  combine_reduce (and its
   LDS-staged variant via pipeline="lds"),
   emu_peer_producer, last_error, version.
 """
@@ -28,6 +29,7 @@ STATUS_TIMEOUT = 1
  TILE_256x128_S3, TILE_128x256_S3, TILE_128x128_S4, TILE_256x256_W8, TILE_256x256_W8_K64) = range(12)
 TILE_PAIRED_ROWS = 0x200  # OR into an explicit tile: pair owner half-blocks with non-owner ones
 TILE_CONSUME_READY = 0x400  # OR into any tile: owner tiles clear the ready_in bits they waited for
+LAMPORT_NOALLOC_BYTES = 32 * 1024 * 1024  # static staging of ar_rmsnorm_lamport_noalloc
 TILE_NAMES = {TILE_256x256: "256x256", TILE_128x256: "128x256", TILE_128x128: "128x128",
               TILE_64x128: "64x128", TILE_32x256: "32x256", TILE_256x256_S4: "256x256_s4",
               TILE_256x128_S3: "256x128_s3", TILE_128x256_S3: "128x256_s3", TILE_128x128_S4: "128x128_s4", TILE_256x256_W8: "256x256_w8",
@@ -79,6 +81,7 @@ def lib():
             "arepi_lamport_prefill": ([vp, i64, vp], i32),
             "arepi_lamport_publish": ([vp, vp, vp, i32, i64, i64, i32, i32, i32, vp], i32),
             "arepi_ar_rmsnorm_lamport": ([vp, vp, vp, i64, i64, i32, f32, i32, u32p, i64, vp], i32),
+            "arepi_ar_rmsnorm_lamport_noalloc": ([vp, vp, i64, i64, i32, f32, i32, u32p, i64, vp, vp], i32),
             "arepi_ar_rmsnorm_lamport_2phase": ([vp, vp, vp, vp, i64, i64, i32, i32, f32, i32, u32p, i64, vp],
                                                 i32),
             "arepi_emu_lamport_phase_a": ([vp, vp, i64, i64, i32, i32, i32, vp], i32),
@@ -379,6 +382,24 @@ def ar_rmsnorm_lamport(staging, gamma, out, eps: float = 1e-6, scope: int = SCOP
         _flags(status, "status", (1,))
     _check(lib().arepi_ar_rmsnorm_lamport(_ptr(staging), _ptr(gamma), _ptr(out), M, N, S, float(eps), scope,
                                           _ptr(status), spin_limit, _stream(stream)), "ar_rmsnorm_lamport")
+
+
+def ar_rmsnorm_lamport_noalloc(gamma, out, S: int, eps: float = 1e-6, scope: int = SCOPE_AGENT, status=None,
+                               spin_limit: int = 0, stream=None) -> int:
+    """ar_rmsnorm_lamport on the library's static staging (no allocation).
+    out is bf16 [M,N] (M = 0 only sets the device up).  Returns the staging's
+    device address on the current device, laid out [S][M][N] for this call,
+    for the producers to publish into."""
+    _bf16(out, "out")
+    M, N = out.shape
+    _bf16(gamma, "gamma", (N,))
+    if status is not None:
+        _flags(status, "status", (1,))
+    addr = ctypes.c_void_p()
+    _check(lib().arepi_ar_rmsnorm_lamport_noalloc(_ptr(gamma), _ptr(out) if M else None, M, N, S, float(eps),
+                                                  scope, _ptr(status), spin_limit, ctypes.byref(addr),
+                                                  _stream(stream)), "ar_rmsnorm_lamport_noalloc")
+    return addr.value
 
 
 # ---- combine --------------------------------------------------------------------------

@@ -24,6 +24,7 @@
 // and eight-wave rows, persistent row loops and a slot-interleaved staging
 // layout all measured slower or equal on MI355X.)
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "arepi_internal.h"
@@ -459,26 +460,28 @@ extern "C" int arepi_lamport_publish(const uint16_t *src, uint16_t *staging, con
     return check_launch("arepi_lamport_publish");
 }
 
-extern "C" int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma, uint16_t *out, int64_t M,
-                                        int64_t N, int S, float eps, int scope, uint32_t *status,
-                                        int64_t spin_limit, arepi_stream_t stream) {
-    auto bad = [](const std::string &m) { return fail(AREPI_EINVAL, "arepi_ar_rmsnorm_lamport: " + m); };
+// Shared validation and launch of the two consumer entry points.
+static int check_consumer(const char *who, int64_t M, int64_t N, int S, float eps, int scope) {
+    auto bad = [who](const std::string &m) { return fail(AREPI_EINVAL, std::string(who) + ": " + m); };
     if (S < 1 || S > 8) return bad("S=" + std::to_string(S) + " outside [1, 8]");
     if (M < 0) return bad("M=" + std::to_string(M) + " must be >= 0");
     if (N < 8 || N % 8) return bad("N=" + std::to_string(N) + " must be a positive multiple of 8");
-    if (N > 16384) return fail(AREPI_EUNSUPPORTED, "arepi_ar_rmsnorm_lamport: N=" + std::to_string(N) + " above 16384");
+    if (N > 16384)
+        return fail(AREPI_EUNSUPPORTED, std::string(who) + ": N=" + std::to_string(N) + " above 16384");
     if (!(eps >= 0.0f)) return bad("eps must be >= 0");
     if (scope != AREPI_SCOPE_AGENT && scope != AREPI_SCOPE_SYSTEM) return bad("scope must be AGENT or SYSTEM");
-    if (M == 0) return ok();
-    if (!staging || !gamma || !out) return bad("staging, gamma and out must be non-NULL");
-    if (!aligned16(staging) || !aligned16(gamma) || !aligned16(out))
-        return bad("staging, gamma and out must be 16-byte aligned");
+    return AREPI_OK;
+}
+
+static int launch_consumer(const char *who, uint16_t *staging, const uint16_t *gamma, uint16_t *out, int64_t M,
+                           int64_t N, int S, float eps, int scope, uint32_t *status, int64_t spin_limit,
+                           hipStream_t s) {
     if (M * N * 2 * 8 > (int64_t)1 << 31)
-        return fail(AREPI_EUNSUPPORTED, "arepi_ar_rmsnorm_lamport: one staging slot (M*N*2 bytes) must be at most 256 MiB");
+        return fail(AREPI_EUNSUPPORTED,
+                    std::string(who) + ": one staging slot (M*N*2 bytes) must be at most 256 MiB");
     const int64_t packs = N / 8;
     const int64_t lim = spin_bound(spin_limit);
     const int sys = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const int ppt = (int)((packs + 255) / 256);
 #define AREPI_RMS_LAUNCH(P, T)                                                                                   \
     hipLaunchKernelGGL((ar_rmsnorm_kernel<P, T>), dim3((unsigned)M), dim3(T), 0, s, staging, gamma, out, M, N, S, \
@@ -492,7 +495,82 @@ extern "C" int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma
     else
         AREPI_RMS_LAUNCH(4, 512);
 #undef AREPI_RMS_LAUNCH
-    return check_launch("arepi_ar_rmsnorm_lamport");
+    return check_launch(who);
+}
+
+extern "C" int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma, uint16_t *out, int64_t M,
+                                        int64_t N, int S, float eps, int scope, uint32_t *status,
+                                        int64_t spin_limit, arepi_stream_t stream) {
+    const char *who = "arepi_ar_rmsnorm_lamport";
+    if (const int rc = check_consumer(who, M, N, S, eps, scope)) return rc;
+    if (M == 0) return ok();
+    if (!staging || !gamma || !out)
+        return fail(AREPI_EINVAL, std::string(who) + ": staging, gamma and out must be non-NULL");
+    if (!aligned16(staging) || !aligned16(gamma) || !aligned16(out))
+        return fail(AREPI_EINVAL, std::string(who) + ": staging, gamma and out must be 16-byte aligned");
+    return launch_consumer(who, staging, gamma, out, M, N, S, eps, scope, status, spin_limit,
+                           reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---- consumer with library-held staging ---------------------------------------
+//
+// For callers that cannot allocate device memory.  The staging is a fixed-size
+// static device array; every GPU the library runs on holds its own copy at its
+// own address.  In host code the array's name is only a host-side stand-in, so
+// host code never hands it to a kernel: the device address is resolved once
+// per device with hipGetSymbolAddress (with that device current) and kept.
+static __device__ __align__(256) uint16_t scratch[AREPI_LAMPORT_NOALLOC_BYTES / 2];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint16_t *g_scratch[kMaxDevices];  // per device: resolved (and armed) address
+}  // namespace
+
+// Address of the current device's staging.  The first call on a device arms
+// the whole array with the sentinel (a fill kernel on `s`); from then on the
+// consumer keeps what it reads armed.
+static int noalloc_staging(const char *who, hipStream_t s, uint16_t **ptr) {
+    int dev = -1;
+    const hipError_t de = hipGetDevice(&dev);
+    if (de != hipSuccess) return fail(AREPI_ELAUNCH, std::string(who) + ": hipGetDevice: " + hipGetErrorString(de));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(AREPI_EUNSUPPORTED, std::string(who) + ": device " + std::to_string(dev) + " beyond 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(AREPI_ELAUNCH, std::string(who) + ": hipGetSymbolAddress(scratch): " + hipGetErrorString(e));
+        constexpr int64_t n16 = AREPI_LAMPORT_NOALLOC_BYTES / 16;
+        hipLaunchKernelGGL(prefill_kernel, dim3(2048), dim3(256), 0, s, static_cast<uint4 *>(p), n16,
+                           static_cast<uint16_t *>(p), (int64_t)0);
+        if (const int rc = check_launch(who)) return rc;
+        g_scratch[dev] = static_cast<uint16_t *>(p);
+    }
+    *ptr = g_scratch[dev];
+    return AREPI_OK;
+}
+
+extern "C" int arepi_ar_rmsnorm_lamport_noalloc(const uint16_t *gamma, uint16_t *out, int64_t M, int64_t N, int S,
+                                                float eps, int scope, uint32_t *status, int64_t spin_limit,
+                                                uint16_t **staging, arepi_stream_t stream) {
+    const char *who = "arepi_ar_rmsnorm_lamport_noalloc";
+    if (const int rc = check_consumer(who, M, N, S, eps, scope)) return rc;
+    const int64_t cap = AREPI_LAMPORT_NOALLOC_BYTES;
+    if (M > cap / ((int64_t)S * N * 2))
+        return fail(AREPI_EUNSUPPORTED, std::string(who) + ": S*M*N*2 = " + std::to_string((int64_t)S * N * 2) +
+                                            "*" + std::to_string(M) + " bytes exceeds the " + std::to_string(cap) +
+                                            "-byte static staging");
+    if (M > 0 && (!gamma || !out)) return fail(AREPI_EINVAL, std::string(who) + ": gamma and out must be non-NULL");
+    if (M > 0 && (!aligned16(gamma) || !aligned16(out)))
+        return fail(AREPI_EINVAL, std::string(who) + ": gamma and out must be 16-byte aligned");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint16_t *st = nullptr;
+    if (const int rc = noalloc_staging(who, s, &st)) return rc;
+    if (staging) *staging = st;
+    if (M == 0) return ok();
+    return launch_consumer(who, st, gamma, out, M, N, S, eps, scope, status, spin_limit, s);
 }
 
 // Shared validation of the two-phase entry points.

@@ -24,8 +24,9 @@
  *     (read it with arepi_last_error(), thread-local).
  *   - Launches are asynchronous on `stream` (a hipStream_t; NULL is the legacy
  *     default stream).  Device-side status words are read by the caller after
- *     synchronising.  The library allocates no device memory and keeps no state
- *     besides the per-thread error message.
+ *     synchronising.  The library allocates no device memory.  Its only state
+ *     is the per-thread error message, a per-device cache of the wall-clock
+ *     rate, and the static staging of arepi_ar_rmsnorm_lamport_noalloc.
  *   - Spin waits are bounded: `spin_limit` > 0 is the number of polls before a
  *     wait gives up; <= 0 selects a deadline of one second of the device's
  *     constant-rate wall clock (s_memrealtime, its rate read from the runtime)
@@ -267,6 +268,35 @@ int arepi_lamport_publish(const uint16_t *src, uint16_t *staging, const int32_t 
 int arepi_ar_rmsnorm_lamport(uint16_t *staging, const uint16_t *gamma, uint16_t *out, int64_t M,
                              int64_t N, int S, float eps, int scope, uint32_t *status,
                              int64_t spin_limit, arepi_stream_t stream);
+
+/* Largest staging (S*M*N*2 bytes) of arepi_ar_rmsnorm_lamport_noalloc: 32 MiB,
+ * e.g. S = 8 slots of up to 292 rows at N = 7168. */
+#define AREPI_LAMPORT_NOALLOC_BYTES (32LL * 1024 * 1024)
+
+/* The consumer above with the staging held by the library, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The staging is a static device
+ * array of AREPI_LAMPORT_NOALLOC_BYTES, one per GPU, laid out as [S][M][N]
+ * for the M, N, S of each call.  The call allocates nothing and calls no
+ * allocating routine.
+ *   - The first call on a device (with that device current) resolves the
+ *     array's address and arms all of it with 0x8000 by a fill kernel on
+ *     `stream`; make that first call outside graph capture (M = 0 does only
+ *     this) and order it before any publication into the array.
+ *   - When `staging` is non-NULL it receives the array's device address on the
+ *     current device: producers publish into it (arepi_lamport_publish, or a
+ *     peer's stores) exactly as into a caller-owned staging.
+ *   - Every call on one GPU shares that GPU's array and it keeps the last
+ *     call's contents: the consumer re-arms every pack it consumes, so it is
+ *     armed again after a call that did not time out.  After a time-out re-arm
+ *     it with arepi_lamport_prefill on the returned address.  Calls that
+ *     overlap on one GPU (two streams, two threads) race on the array.
+ * gamma, out, M, N, S, eps, scope, status, spin_limit are as in
+ * arepi_ar_rmsnorm_lamport.  S*M*N*2 above AREPI_LAMPORT_NOALLOC_BYTES is
+ * refused with AREPI_EUNSUPPORTED before anything is launched. */
+int arepi_ar_rmsnorm_lamport_noalloc(const uint16_t *gamma, uint16_t *out, int64_t M, int64_t N, int S,
+                                     float eps, int scope, uint32_t *status, int64_t spin_limit,
+                                     uint16_t **staging, arepi_stream_t stream);
 
 /* Two-phase form (same page, Approach: "phase A" is the reduce-scatter with
  * cross-device stores, "phase B" the consumer; Correctness notes: every block

@@ -207,6 +207,24 @@ def test_lamport_and_combine_validate_before_launch():
     assert "items_per_release" in A.last_error()
 
 
+def test_noalloc_consumer_refuses_sizes_beyond_its_static_staging():
+    """The limit is checked before any device call: the row just past it is
+    refused as unsupported, the largest row count that fits passes the size
+    check and then fails on the NULL pointers."""
+    L = A.lib()
+    S, N = 8, 7168
+    rows = A.LAMPORT_NOALLOC_BYTES // (S * N * 2)
+    assert rows == 292
+    rc = L.arepi_ar_rmsnorm_lamport_noalloc(None, None, rows + 1, N, S, 1e-6, 0, None, 0, None, None)
+    assert rc == A.EUNSUPPORTED and "static staging" in A.last_error()
+    rc = L.arepi_ar_rmsnorm_lamport_noalloc(None, None, rows, N, S, 1e-6, 0, None, 0, None, None)
+    assert rc == A.EINVAL and "non-NULL" in A.last_error()
+    rc = L.arepi_ar_rmsnorm_lamport_noalloc(None, None, 4, 64, 9, 1e-6, 0, None, 0, None, None)
+    assert rc == A.EINVAL and "S=9" in A.last_error()
+    rc = L.arepi_ar_rmsnorm_lamport_noalloc(None, None, 1 << 40, 16384, 8, 1e-6, 0, None, 0, None, None)
+    assert rc == A.EUNSUPPORTED  # no overflow in the size check
+
+
 def test_binding_checks_dtype_before_pointers():
     import torch
     x = torch.zeros(4, 8, dtype=torch.float32)
