@@ -87,8 +87,9 @@ def lib():
             "arepi_emu_lamport_phase_a": ([vp, vp, i64, i64, i32, i32, i32, vp], i32),
             "arepi_combine_reduce": ([vp, vp, vp, i64, i32, i64, vp], i32),
             "arepi_combine_reduce_lds": ([vp, vp, vp, i64, i32, i64, vp], i32),
-            "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp],
-                                        i32),
+            "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp,
+                                         vp], i32),
+            "arepi_emu_producer_gate": ([vp, u32p, i64, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -325,10 +326,11 @@ def gemm_rs_fp8(x, xs, wt, ws, recv, ready_in, out, R: int, owner: int, send=Non
 
 def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N: int,
                       flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT,
-                      workgroups: int = 0, items_per_release: int = 1, stream=None):
+                      workgroups: int = 0, items_per_release: int = 1, resident=None, stream=None):
     """Test-only: land (peer, tile) items of src[p] into recv[p] and set their bits,
     items_per_release tiles per release (workgroups > 0: that many batches in
-    flight at a time)."""
+    flight at a time).  resident: int32 [2] (zero before first use) for
+    emu_producer_gate."""
     seg = M // R
     torch = _torch()
     _need(order, "order", (torch.int32,))
@@ -336,6 +338,8 @@ def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N:
         raise ValueError("order must be int32 [n_items, 2]")
     words = gemm_rs_flag_words(M, N, R, flag_tile_m, flag_tile_n)
     _flags(ready_in, "ready_in", (R, words))
+    if resident is not None:
+        _flags(resident, "resident", (2,))
     sp = (ctypes.c_void_p * R)()
     rp = (ctypes.c_void_p * R)()
     for p in range(R):
@@ -348,8 +352,19 @@ def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N:
     rc = lib().arepi_emu_peer_producer(ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p),
                                        _ptr(ready_in), _ptr(order), order.shape[0], M, N, R, owner,
                                        flag_tile_m, flag_tile_n, scope, workgroups, items_per_release,
-                                       _stream(stream))
+                                       _ptr(resident), _stream(stream))
     _check(rc, "emu_peer_producer")
+
+
+def emu_producer_gate(resident, status=None, spin_limit: int = 0, stream=None):
+    """Test-only: on the consumer's stream, between emu_peer_producer (issued
+    first, with the same resident) and the consumer: returns once every
+    producer workgroup has started, so the consumer cannot crowd it out."""
+    _flags(resident, "resident", (2,))
+    if status is not None:
+        _flags(status, "status", (1,))
+    _check(lib().arepi_emu_producer_gate(_ptr(resident), _ptr(status), spin_limit, _stream(stream)),
+           "emu_producer_gate")
 
 
 # ---- Lamport AR + RMSNorm ------------------------------------------------------------

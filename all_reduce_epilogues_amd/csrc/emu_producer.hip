@@ -25,6 +25,7 @@ struct EmuParams {
     int64_t n_items, seg, N, ftiles_n, ftiles, fwords;
     int ftm, ftn, R, owner, system_scope;
     int per_release;  // items landed per release
+    uint32_t *resident;  // NULL, or [2]: workgroups started, grid size
 };
 
 __device__ bool item_valid(const EmuParams &p, const int64_t item, int &peer, int64_t &t) {
@@ -81,10 +82,15 @@ __device__ void copy_item(const EmuParams &p, const int64_t item) {
 // lands batches g, g + G, g + 2G, ... (G = grid size), so a grid smaller than
 // the batch count paces the landing like a link of bounded rate.  Each batch:
 // copies, drain, barrier, one release, then its bits.
-// Its waves share CUs with the GEMM it feeds, whose owner tiles spin on these
-// bits: 73 VGPRs here, and two waves of the 214-VGPR headline GEMM tile leave
-// 80 per SIMD lane.
+// Its waves share the GPU with the GEMM it feeds, whose owner tiles spin on
+// these bits; a workgroup never waits, so once it is resident it finishes.
+// With `resident` given, every workgroup announces itself on arrival, so that
+// emu_gate_kernel can hold the consumer back until the whole grid has started.
 __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
+    if (p.resident && threadIdx.x == 0) {
+        __hip_atomic_store(p.resident + 1, gridDim.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(p.resident, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     const int64_t K = p.per_release, batches = (p.n_items + K - 1) / K;
     for (int64_t j = blockIdx.x; j < batches; j += gridDim.x) {
         const int64_t i0 = j * K, i1 = min(i0 + K, p.n_items);
@@ -104,6 +110,32 @@ __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
     }
 }
 
+// One wave, launched on the consumer's stream between the producer and the
+// consumer: waits until every producer workgroup has started (resident[0]
+// reaches the grid size in resident[1]), then returns the pair to zero.  The
+// consumer is queued behind it, so it cannot take the compute units before
+// the producer holds its own; the producer never waits, so it then finishes
+// whatever the consumer's workgroups occupy.
+__global__ void __launch_bounds__(64) emu_gate_kernel(uint32_t *resident, uint32_t *status, int64_t spin_limit) {
+    if (threadIdx.x != 0) return;
+    int64_t n = 0;
+    const uint64_t t0 = spin_clock();
+    for (;;) {
+        const uint32_t g = load_relaxed(resident + 1, false);
+        const uint32_t c = load_relaxed(resident, false);
+        if (g != 0 && c >= g) {
+            __hip_atomic_fetch_sub(resident, g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(resident + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        if (spin_expired(spin_limit, n, t0)) {
+            if (status) atomicOr(status, (uint32_t)AREPI_STATUS_TIMEOUT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 }  // namespace
 }  // namespace arepi
 
@@ -112,7 +144,8 @@ using namespace arepi;
 extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
                                        const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
                                        int owner, int flag_tile_m, int flag_tile_n, int scope,
-                                       int workgroups, int items_per_release, arepi_stream_t stream) {
+                                       int workgroups, int items_per_release, uint32_t *resident,
+                                       arepi_stream_t stream) {
     auto bad = [](const std::string &m) { return fail(AREPI_EINVAL, "arepi_emu_peer_producer: " + m); };
     if (R < 1 || R > kMaxR) return bad("R=" + std::to_string(R) + " outside [1, 8]");
     if (owner < 0 || owner >= R) return bad("owner outside [0, R-1]");
@@ -148,9 +181,20 @@ extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *con
     p.owner = owner;
     p.system_scope = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
     p.per_release = items_per_release;
+    p.resident = resident;
     const int64_t batches = (n_items + items_per_release - 1) / items_per_release;
     const int64_t groups = workgroups == 0 ? batches : std::min<int64_t>(workgroups, batches);
     hipLaunchKernelGGL(emu_producer_kernel, dim3((unsigned)groups), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), p);
     return check_launch("arepi_emu_peer_producer");
+}
+
+extern "C" int arepi_emu_producer_gate(uint32_t *resident, uint32_t *status, int64_t spin_limit,
+                                       arepi_stream_t stream) {
+    if (!resident) return fail(AREPI_EINVAL, "arepi_emu_producer_gate: resident must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(resident) & 7u)
+        return fail(AREPI_EINVAL, "arepi_emu_producer_gate: resident must be 8-byte aligned");
+    hipLaunchKernelGGL(emu_gate_kernel, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), resident,
+                       status, spin_bound(spin_limit));
+    return check_launch("arepi_emu_producer_gate");
 }

@@ -5,6 +5,8 @@ the tp=4 share -- X [4096,2048] . W [2048,4096] bf16, R=4, owner segment of 1024
 rows, three peer partials landed per 128x128 flag tile by an emulated-peer
 producer on a second stream in shuffled order, their ready bits published
 eight tiles per release -- as TFLOP/s of the whole step (2*M*N*K per step).
+Each step queues the producer, then a one-wave gate on the GEMM's stream
+that waits until every producer workgroup has started, then the GEMM.
 The same step with one release per tile is reported beside it in `config`.
 Inputs are resident in HBM before timing starts.
 
@@ -54,6 +56,10 @@ LAMPORT2_BYTES = 5 * P_4096x7168 + 7168 * 2
 # the L2 the GEMM is using -- which a remote peer's release never does to this
 # GPU.  The step with one release per tile is reported beside the headline.
 PRODUCER_TILES_PER_RELEASE = 8
+# The producer lands its batches with 96 workgroups at a time (a link of
+# bounded rate).  The gate between the producer and the GEMM waits until all
+# of them have started, so a small persistent grid also keeps the gate short.
+PRODUCER_WORKGROUPS = 96
 
 LEGS = ("gemm_rs", "gemm_rs_tiny", "gemm_rs_prestaged", "gemm_rs_tp8", "lamport", "combine", "combine_lds",
         "lamport_2phase", "gemm_rs_fp8", "gemm_rs_ring", "gemm_rs_ring_prestaged")
@@ -183,7 +189,8 @@ def _ready_all(torch, R, absent, words, tiles):
     return torch.from_numpy(full.view(np.int32)).to(torch.device("cuda:0"))
 
 
-def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs=0, per_release=1):
+def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs=PRODUCER_WORKGROUPS,
+                       per_release=1):
     """tp=4 share; a producer stream lands the peers while the GEMM runs
     (ring=True: the push-ring hop, the producer landing the upstream partials).
 
@@ -192,7 +199,10 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
     zero again when it ends and needs no clearing kernel.  The producer of step
     i, on the side stream, waits for GEMM i-1 to end (it reuses recv and
     ready_in) and then runs while GEMM i does; GEMM i's owner tiles wait for
-    its bits.  ready_out is only ever OR-ed into.
+    its bits.  Between the two GEMMs the main stream holds a one-wave gate
+    that returns once every producer workgroup of step i has started, so GEMM
+    i cannot take the compute units the producer needs.  ready_out is only
+    ever OR-ed into.
 
     Returns the wall time per step and the GEMM's average launch duration from
     HIP events recorded on its stream just before and after each launch.
@@ -219,6 +229,7 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
     out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
     send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    resident = torch.zeros(2, dtype=torch.int32, device=dev)
     main = torch.cuda.current_stream()
     side = side_stream(torch)
     tile = (A.gemm_rs_ring_pick_tile if ring else A.gemm_rs_pick_tile)(M, N, K, R, owner, publish=True)
@@ -231,7 +242,8 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
         if i > 0:
             H.wait(side, ev_ge[i - 1])
         A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, absent, M, N, workgroups=producer_wgs,
-                            items_per_release=per_release, stream=side)
+                            items_per_release=per_release, resident=resident, stream=side)
+        A.emu_producer_gate(resident, status=status, stream=main)
         H.record(ev_gs[i], main)
         if ring:
             A.gemm_rs_ring(x, w, recv, rin, out, send, R, owner, ready_out=rout,
@@ -603,10 +615,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": "gemm_rs tp4 share: X[4096,2048] x W[2048,4096] bf16, R=4, owner=0, "
                                "3 peer partials [1024,4096] landed per 128x128 flag tile by a producer "
-                               "stream in shuffled order, their bits published 8 tiles per release; "
+                               "stream (96 workgroups) in shuffled order, their bits published 8 tiles per "
+                               "release; a gate holds the GEMM until every producer workgroup has started; "
                                "send + ready_out published",
                    "M": 4096, "N": 4096, "K": 2048, "R": 4, "owner": 0,
                    "producer_tiles_per_release": PRODUCER_TILES_PER_RELEASE,
+                   "producer_workgroups": PRODUCER_WORKGROUPS,
                    "tile": head["tile"] if head else None},
     }
     if head:

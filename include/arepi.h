@@ -359,13 +359,32 @@ int arepi_combine_reduce_lds(const uint16_t *x, const float *gate, uint16_t *out
  * (one workgroup each); workgroups = G > 0 lands them G at a time, in order,
  * which paces the arrivals like a link of bounded rate and leaves the other
  * compute units to the consumer.
+ * resident: NULL, or a device uint32 [2] (zero before first use) through
+ * which every producer workgroup announces its start, for
+ * arepi_emu_producer_gate.
  * Errors: EINVAL for bad shapes, NULL pointers, workgroups < 0 or
  * items_per_release < 1.
  * ------------------------------------------------------------------------ */
 int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
                             const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
                             int owner, int flag_tile_m, int flag_tile_n, int scope, int workgroups,
-                            int items_per_release, arepi_stream_t stream);
+                            int items_per_release, uint32_t *resident, arepi_stream_t stream);
+
+/* Test-only forward-progress gate for a consumer that waits on the emulated
+ * producer on the same GPU (the aiter PR #4977 Correctness notes: producer
+ * work must not be left unscheduled behind spinning consumers).  Launch it on
+ * the consumer's stream after the producer (issued with the same `resident`)
+ * and before the consumer: one wave waits until every producer workgroup has
+ * started, then zeroes resident for the next step.  The producer never
+ * waits, so once resident it finishes, whatever registers the consumer's
+ * workgroups take.  Issue the producer first in host order: when the two
+ * streams share one hardware queue, the queue then runs producer, gate and
+ * consumer in turn.  The next producer on the same `resident` must be
+ * ordered after this gate.  The wait is bounded by spin_limit (encoding as
+ * above); on expiry AREPI_STATUS_TIMEOUT is ORed into *status (status may be
+ * NULL) and resident is left as it is. */
+int arepi_emu_producer_gate(uint32_t *resident, uint32_t *status, int64_t spin_limit,
+                            arepi_stream_t stream);
 
 /* Test-only: phase A of the two-phase Lamport call for rank `rank` alone
  * (stands in for a peer GPU's phase A on one GPU).  Same arguments and

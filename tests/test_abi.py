@@ -202,9 +202,11 @@ def test_lamport_and_combine_validate_before_launch():
     assert L.arepi_combine_reduce(None, None, None, 4, 8, 60, None) == A.EINVAL
     assert L.arepi_combine_reduce(None, None, None, 0, 8, 64, None) == A.OK  # empty: nothing to do
     assert L.arepi_combine_reduce(None, None, None, 4, 8, 64, None) == A.EINVAL
-    assert L.arepi_emu_peer_producer(None, None, None, None, 1, 256, 512, 2, 5, 128, 128, 0, 0, 1, None) == A.EINVAL
-    assert L.arepi_emu_peer_producer(None, None, None, None, 1, 256, 512, 2, 0, 128, 128, 0, 0, 0, None) == A.EINVAL
+    assert L.arepi_emu_peer_producer(None, None, None, None, 1, 256, 512, 2, 5, 128, 128, 0, 0, 1, None, None) == A.EINVAL
+    assert L.arepi_emu_peer_producer(None, None, None, None, 1, 256, 512, 2, 0, 128, 128, 0, 0, 0, None, None) == A.EINVAL
     assert "items_per_release" in A.last_error()
+    assert L.arepi_emu_producer_gate(None, None, 0, None) == A.EINVAL
+    assert "resident" in A.last_error()
 
 
 def test_noalloc_consumer_refuses_sizes_beyond_its_static_staging():

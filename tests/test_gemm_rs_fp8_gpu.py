@@ -135,7 +135,9 @@ def test_tp4_share_prestaged_and_concurrent_producer():
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     side = torch.cuda.Stream()
-    A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, stream=side)
+    resident = torch.zeros(2, dtype=torch.int32, device=device())
+    A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, resident=resident, stream=side)
+    A.emu_producer_gate(resident, status=status, stream=torch.cuda.current_stream())
     conc = run(case, ready_in=rin, recv_dev=recv, status=status, tile=A.TILE_CONSUME_READY,
                stream=torch.cuda.current_stream())
     assert int(status.item()) == 0

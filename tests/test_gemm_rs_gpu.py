@@ -198,13 +198,65 @@ def test_tp4_workload_prestaged_and_concurrent_producer():
         torch.cuda.synchronize()
         side = torch.cuda.Stream()
         main = torch.cuda.current_stream()
+        resident = torch.zeros(2, dtype=torch.int32, device=dev)
         A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, workgroups=groups,
-                            items_per_release=per_release, stream=side)
+                            items_per_release=per_release, resident=resident, stream=side)
+        A.emu_producer_gate(resident, status=status, stream=main)
         A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, status=status, stream=main)
         torch.cuda.synchronize()
         assert int(status.item()) == 0, "a readiness wait timed out"
         assert np.array_equal(from_dev_bf16(out), pre["out"]), "result depends on arrival order"
         assert np.array_equal(from_dev_u32(rin), flag_words_all_set(R, owner, tiles))
+
+
+def test_gate_lets_the_producer_finish_beside_a_register_full_gemm():
+    """The 4-wave 256x256 tile at R = 4 allocates all 512 registers per SIMD
+    lane, so no producer wave fits beside it on a compute unit.  The gate,
+    queued between the producer and the GEMM, holds the GEMM back until every
+    producer workgroup has started; the producer never waits, so every
+    owner-tile wait is met and the result equals the pre-staged one.  The gate
+    leaves resident at zero for the next step."""
+    case = inputs.workload_gemm_rs(2)
+    M, N, R, owner = case["M"], case["N"], case["R"], case["owner"]
+    seg = M // R
+    dev = device()
+    pre = run(case, tile=A.TILE_256x256)
+    tiles = oracle.flag_tiles(M, N, R, 128, 128)
+    x, w = to_dev_bf16(case["x"]), to_dev_bf16(case["w"])
+    src = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
+    resident = torch.zeros(2, dtype=torch.int32, device=dev)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for seed, groups in ((21, 16), (22, 0)):
+        print("gate seed %d workgroups %d" % (seed, groups), flush=True)
+        order = torch.from_numpy(inputs.producer_order(R, owner, tiles, seed)).to(dev)
+        recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
+        rin = torch.zeros((R, A.gemm_rs_flag_words(M, N, R)), dtype=torch.int32, device=dev)
+        out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
+        send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        rout = torch.zeros_like(rin)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, workgroups=groups, resident=resident,
+                            stream=side)
+        A.emu_producer_gate(resident, status=status, stream=main)
+        A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=A.TILE_256x256,
+                        status=status, stream=main)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, "a wait timed out"
+        assert np.array_equal(from_dev_bf16(out), pre["out"])
+        assert not resident.any().item(), "the gate must leave resident at zero"
+
+
+def test_gate_times_out_when_no_producer_announces():
+    """Nothing ever starts on `resident`: the gate's bounded wait gives up,
+    reports the time-out and finishes."""
+    dev = device()
+    resident = torch.zeros(2, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    A.emu_producer_gate(resident, status=status, spin_limit=2000)
+    torch.cuda.synchronize()
+    assert int(status.item()) & A.STATUS_TIMEOUT
 
 
 @pytest.mark.parametrize("M,owner", [(256, 0), (1024, 0), (1024, 7), (4096, 0), (8192, 0)])
@@ -254,6 +306,7 @@ def test_consume_ready_leaves_ready_in_clear_for_the_next_call(M, N, K, R, owner
     recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
     rin = torch.zeros((R, A.gemm_rs_flag_words(M, N, R, ftm, ftn)), dtype=torch.int32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
+    resident = torch.zeros(2, dtype=torch.int32, device=dev)
     side = torch.cuda.Stream()
     main = torch.cuda.current_stream()
     for call, seed in enumerate((31, 32)):
@@ -267,7 +320,8 @@ def test_consume_ready_leaves_ready_in_clear_for_the_next_call(M, N, K, R, owner
         order = torch.from_numpy(inputs.producer_order(R, owner, tiles, seed)).to(dev)
         torch.cuda.synchronize()
         A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, flag_tile_m=ftm, flag_tile_n=ftn,
-                            workgroups=16 * call, stream=side)
+                            workgroups=16 * call, resident=resident, stream=side)
+        A.emu_producer_gate(resident, status=status, stream=main)
         A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, flag_tile_m=ftm,
                         flag_tile_n=ftn, tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
         torch.cuda.synchronize()

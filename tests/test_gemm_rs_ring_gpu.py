@@ -209,7 +209,10 @@ def test_tp4_workload_prestaged_and_concurrent_producer():
         torch.cuda.synchronize()
         side = torch.cuda.Stream()
         main = torch.cuda.current_stream()
-        A.emu_peer_producer(src, up, rin, order, R, chain, M, N, workgroups=groups, stream=side)
+        resident = torch.zeros(2, dtype=torch.int32, device=dev)
+        A.emu_peer_producer(src, up, rin, order, R, chain, M, N, workgroups=groups, resident=resident,
+                            stream=side)
+        A.emu_producer_gate(resident, status=status, stream=main)
         A.gemm_rs_ring(x, w, up, rin, out, send, R, owner, status=status, stream=main)
         torch.cuda.synchronize()
         assert int(status.item()) == 0, "a readiness wait timed out"
@@ -255,7 +258,10 @@ def test_consume_ready_leaves_ready_in_clear():
         rout = torch.zeros_like(rin)
         order = torch.from_numpy(inputs.producer_order(R, chain, tiles, seed)).to(dev)
         torch.cuda.synchronize()
-        A.emu_peer_producer(src, up, rin, order, R, chain, M, N, workgroups=16 * call, stream=side)
+        resident = torch.zeros(2, dtype=torch.int32, device=dev)
+        A.emu_peer_producer(src, up, rin, order, R, chain, M, N, workgroups=16 * call, resident=resident,
+                            stream=side)
+        A.emu_producer_gate(resident, status=status, stream=main)
         A.gemm_rs_ring(x, w, up, rin, out, send, R, owner, ready_out=rout, tile=A.TILE_CONSUME_READY,
                        status=status, stream=main)
         torch.cuda.synchronize()
