@@ -627,24 +627,30 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         // block b, s_b/s_{b+1} (or s_last after the last block), one per scale
         // block, into fac buffer b&1; the barrier that ends the step publishes
         // them.  One reciprocal per row and K block and one per scale block.
-        // Rows past M and scale
-        // blocks past N get factor 1 (their products are zero).
+        // Rows past M and scale blocks past N get factor 1 (their products
+        // are zero).  A zero scale (what a quantiser emits for an all-zero
+        // block, e.g. padding rows) is not taken as the running unit: the
+        // unit in effect carries over it (factor 1 across the block), so a
+        // zero-scale block whose fp8 data are zero adds nothing, as in the
+        // plain block sum, and the ratios stay finite.  Before the first
+        // non-zero scale the unit is 1.
         const int64_t frow = tid < BM ? row_of(tid) : -1;
-        float rs = frow >= 0 ? p.xs[frow * KB] : 1.0f;
+        auto unit = [](float raw, float carried) { return raw != 0.0f ? raw : carried; };
+        float rs = frow >= 0 ? unit(p.xs[frow * KB], 1.0f) : 1.0f;
         float cs[NCB];
 #pragma unroll
-        for (int c = 0; c < NCB; ++c) cs[c] = nb + c < NBW ? p.ws[(int64_t)(nb + c) * KB] : 1.0f;
+        for (int c = 0; c < NCB; ++c) cs[c] = nb + c < NBW ? unit(p.ws[(int64_t)(nb + c) * KB], 1.0f) : 1.0f;
         asm volatile("" ::"v"(rs), "v"(cs[0]), "v"(cs[NCB - 1]));  // the loads land before the first direct-to-LDS load
         auto write_factor = [&](int b) {
             if (tid < BM) {
                 const float *sc = reinterpret_cast<const float *>(smem + LDS_BYTES + (b % S) * SCL);
                 const bool more = b + 1 < KB;
-                const float rn = more && frow >= 0 ? sc[tid] : 1.0f;
+                const float rn = more && frow >= 0 ? unit(sc[tid], rs) : 1.0f;
                 // ratios through v_rcp_f32 (within 1 ulp; exact for powers of two)
                 const float rr = more ? rs * __builtin_amdgcn_rcpf(rn) : rs;
 #pragma unroll
                 for (int c = 0; c < NCB; ++c) {
-                    const float cn = more && nb + c < NBW ? sc[256 + c] : 1.0f;
+                    const float cn = more && nb + c < NBW ? unit(sc[256 + c], cs[c]) : 1.0f;
                     fac[((b & 1) * NCB + c) * BM + tid] = rr * (more ? cs[c] * __builtin_amdgcn_rcpf(cn) : cs[c]);
                     cs[c] = cn;
                 }
@@ -828,15 +834,6 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     }
     };
 
-    // Peer combine on the matrix cores.  For every 32-row accumulator block
-    // holding owner rows, each peer's partial P (bf16, ascending rank order) is
-    // added as acc += P[:, 0:16] x I[0:16, :] + P[:, 16:32] x I[16:32, :]: each
-    // output element receives exactly one nonzero product p x 1.0 (exact), so
-    // the result is the fp32 sum acc + p rounded once, peer after peer, as a
-    // vector add would give it.  P is loaded straight into the MFMA A-operand
-    // layout (lane l: row l%32, 8 consecutive columns); rows that are not owner
-    // rows, columns past N and slots past R-1 load zeros (out-of-range buffer
-    // offsets), adding +0.0.
     const int wm_u = wave_u / NWN;
     // Chunk (hb: false = A, true = B) and row inside it of this wave's row
     // wm*WM + t (t < WM, a multiple of 8).  When WM is a multiple of 2*IL the

@@ -17,12 +17,14 @@
 // consumer reads each pack once with a plain 16-byte load and only polls
 // coherently (sc1 loads) when the pack still shows a sentinel.
 //
-// Consumer layout: one 256-thread workgroup per row; thread t owns packs t,
-// t+256, ... of the row (coalesced 16-byte columns; 3-4 each at N=7168), keeps
-// the fp32 slot sums of its packs in registers, reduces sum(s^2) across the
-// workgroup (wave shuffles, then LDS), and writes the normalised row.  (Two-
-// and eight-wave rows, persistent row loops and a slot-interleaved staging
-// layout all measured slower or equal on MI355X.)
+// Consumer layout: one workgroup of NT threads per row; thread t owns packs
+// t, t+NT, ... of the row (coalesced 16-byte columns, PPT of them), keeps the
+// fp32 slot sums of its packs in registers, reduces sum(s^2) across the
+// workgroup (wave shuffles, then LDS), and writes the normalised row.  The
+// launch takes NT = 256 with one pack per thread up to 256 packs (N <= 2048),
+// NT = 512 with two up to 1024 packs (N = 7168: 896 packs), and NT = 512
+// with four above that.  (Other row widths, persistent row loops and a
+// slot-interleaved staging layout measured slower or equal on MI355X.)
 #include <algorithm>
 #include <mutex>
 #include <string>

@@ -216,9 +216,14 @@ int arepi_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const uint16_t *con
  * d_b, out = t_last * s_last), and by its re-review finding that the gfx950
  * matrix atom reads OCP e4m3fn bytes.
  *   x   e4m3fn bytes [M,K]            X_r
- *   xs  fp32 [M][K/128]               row-major; must be > 0 and finite
+ *   xs  fp32 [M][K/128]               row-major, finite
  *   wt  e4m3fn bytes [N,K]            W_r TRANSPOSED (K contiguous)
- *   ws  fp32 [ceil(N/128)][K/128]     row-major; must be > 0 and finite
+ *   ws  fp32 [ceil(N/128)][K/128]     row-major, finite
+ * A zero scale is accepted for a block whose fp8 data are all zero (what a
+ * quantiser emits for an all-zero block, e.g. padding rows): the block adds
+ * nothing, and the running rescale carries the previous non-zero scale
+ * across it.  A zero scale over non-zero data, and non-finite scales, give
+ * unspecified outputs.
  * The reduce-scatter epilogue and every other argument are those of
  * arepi_gemm_rs_fused (direct sum over the R-1 peers).  The compute tile is
  * 256x256 (tile_cfg may only carry AREPI_TILE_CONSUME_READY; with ready_out,

@@ -88,6 +88,33 @@ def test_matches_oracle(M, N, K, R, owner, ftm, ftn):
     check(case, res, ftm, ftn, what="fp8 %s" % ((M, N, K, R, owner),))
 
 
+def test_zero_scale_blocks_with_zero_data_add_nothing():
+    """A quantiser gives an all-zero block a zero scale.  Such blocks (the
+    first, a middle and the last K block of some rows; every block of one row;
+    a -0.0 scale; a zero column-block scale) must add nothing, as in the
+    oracle's plain sum of s_b * d_b, and leave the other blocks' sum finite."""
+    M, N, K, R, owner = 512, 1032, 512, 4, 1
+    case = inputs.gemm_rs_fp8_case(M, N, K, R, owner=owner, seed=81)
+    x, xs, wt, ws = case["x"].copy(), case["xs"].copy(), case["wt"].copy(), case["ws"].copy()
+    seg = M // R
+    zero_blocks = {seg + 0: [0], seg + 5: [2], seg + 9: [3], seg + 17: [0, 1, 2, 3], 3: [1], 300: [0, 3]}
+    for row, blocks in zero_blocks.items():
+        for b in blocks:
+            xs[row, b] = 0.0
+            x[row, b * 128:(b + 1) * 128] = 0
+    xs[seg + 33, 2] = -0.0
+    x[seg + 33, 256:384] = 0
+    ws[1, 3] = 0.0          # columns 128..255, last K block
+    wt[128:256, 384:512] = 0
+    ws[8, 0] = 0.0          # the ragged last column block (1024..1031), first K block
+    wt[1024:1032, 0:128] = 0
+    case.update(x=x, xs=xs, wt=wt, ws=ws)
+    res = run(case)
+    check(case, res, what="fp8 zero-scale blocks")
+    out = (res["out"].astype(np.uint32) << 16).view(np.float32)
+    assert np.isfinite(out).all()
+
+
 def test_all_ones_two_ranks_golden():
     g = read_golden("fp8_one_encodings.txt")
     M, N, K, R = g["M"], g["N"], g["K"], g["ranks"]
