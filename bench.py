@@ -411,7 +411,8 @@ def lamport_2phase(A, inputs, torch, iters, warmup, case):
     t = st["ms_median"] * 1e-3
     return dict(**st, gbs=LAMPORT2_BYTES / t / 1e9, frac_hbm=LAMPORT2_BYTES / t / 1e9 / PEAK_HBM_GBS,
                 R=R, M=M, N=N, roofline=roofline("hbm", LAMPORT2_BYTES, st, PEAK_HBM_GBS, "GB/s",
-                                                 None, "lamport2_kernel"))
+                                                 measured_traffic("lamport_2phase", "rank0of8"),
+                                                 "lamport2_kernel"))
 
 
 def combine(A, inputs, torch, iters, warmup, case, pipeline="registers"):
@@ -485,12 +486,14 @@ CSRC = os.path.join(HERE, "all_reduce_epilogues_amd", "csrc")
 # counter record per workload: file under profiles/ and the kernel sources it was
 # measured on (the record goes stale when one of them changes)
 COUNTERS = {
-    "gemm_rs_tp4": ("gemm_rs_tp4_counters.txt", ("gemm_rs_impl.h", "gemm_rs.hip")),
-    "gemm_rs_tp8_m256": ("gemm_rs_tp8_m256_counters.txt", ("gemm_rs_impl.h", "gemm_rs.hip")),
-    "gemm_rs_tp8_m8192": ("gemm_rs_tp8_m8192_counters.txt", ("gemm_rs_impl.h", "gemm_rs.hip")),
+    "gemm_rs_tp4": ("gemm_rs_tp4_counters.txt", ("gemm_rs_impl.h", "gemm_rs_kernel.h", "gemm_rs.hip")),
+    "gemm_rs_tp8_m256": ("gemm_rs_tp8_m256_counters.txt",
+                         ("gemm_rs_impl.h", "gemm_rs_kernel.h", "gemm_rs.hip", "gemm_rs_mixed.hip")),
+    "gemm_rs_tp8_m8192": ("gemm_rs_tp8_m8192_counters.txt", ("gemm_rs_impl.h", "gemm_rs_kernel.h", "gemm_rs.hip")),
     "lamport": ("lamport_counters.txt", ("lamport.hip",)),
     "combine": ("combine_counters.txt", ("combine.hip",)),
     "combine_lds": ("combine_counters_lds.txt", ("combine.hip",)),
+    "lamport_2phase": ("lamport_2phase_counters.txt", ("lamport.hip",)),
 }
 COUNTERS_FILE = None   # (tests) one record file used for every key instead
 
