@@ -1133,9 +1133,9 @@ constexpr TileCfg kTiles[] = {
     {AREPI_TILE_256x256_S4, 256, 256, 1, 1.00},
     {AREPI_TILE_256x256, 256, 256, 1, 0.96},
     {AREPI_TILE_256x128_S3, 256, 128, 2, 0.95},
+    {AREPI_TILE_128x256, 128, 256, 1, 0.97},
     {AREPI_TILE_128x256_S3, 128, 256, 2, 0.93},
     {AREPI_TILE_128x128_S4, 128, 128, 2, 0.80},
-    {AREPI_TILE_128x256, 128, 256, 1, 0.80},
     {AREPI_TILE_128x128, 128, 128, 2, 0.75},
     {AREPI_TILE_64x128, 64, 128, 3, 0.60},
     {AREPI_TILE_32x256, 32, 256, 2, 0.40},

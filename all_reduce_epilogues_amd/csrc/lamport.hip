@@ -285,14 +285,13 @@ __global__ void __launch_bounds__(NT) lamport2_kernel(const Lamport2Params p) {
     const uint32_t plane2 = (uint32_t)(p.M * p.N * 2);
 
     // ---- phase A ----
-    for (int64_t k = a0 + (int64_t)blockIdx.x * NT + tid; k < a1; k += (int64_t)gridDim.x * NT) {
+    // Two packs per thread and iteration (the second one GS packs further),
+    // so each thread has 2R loads in flight.
+    const int64_t GS = (int64_t)gridDim.x * NT;
+    auto reduce_pack = [&](const uint4 (&v)[kMaxRanks]) {
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-        uint4 v[kMaxRanks];
-#pragma unroll
-        for (int r = 0; r < kMaxRanks; ++r)
-            if (r < p.R) v[r] = load16_nt(p.in[r] + k * 8);
 #pragma unroll
         for (int r = 0; r < kMaxRanks; ++r)
             if (r < p.R) {
@@ -303,6 +302,9 @@ __global__ void __launch_bounds__(NT) lamport2_kernel(const Lamport2Params p) {
             }
         const uint4 t = pack8(acc);
         const i32x4 c = {(int)canon2(t.x), (int)canon2(t.y), (int)canon2(t.z), (int)canon2(t.w)};
+        return c;
+    };
+    auto store_pack = [&](const i32x4 c, int64_t k) {
 #pragma unroll
         for (int d = 0; d < kMaxRanks; ++d)
             if (d < p.R) {
@@ -313,6 +315,20 @@ __global__ void __launch_bounds__(NT) lamport2_kernel(const Lamport2Params p) {
                 else
                     __builtin_amdgcn_raw_buffer_store_b128(c, rs, (uint32_t)(k * 16), 0, kAuxCoherentAgent);
             }
+    };
+    for (int64_t k = a0 + (int64_t)blockIdx.x * NT + tid; k < a1; k += 2 * GS) {
+        const bool two = k + GS < a1;
+        const int64_t k2 = two ? k + GS : k;  // (clamped: loaded, never stored)
+        uint4 v[kMaxRanks], w[kMaxRanks];
+#pragma unroll
+        for (int r = 0; r < kMaxRanks; ++r)
+            if (r < p.R) {
+                v[r] = load16_nt(p.in[r] + k * 8);
+                w[r] = load16_nt(p.in[r] + k2 * 8);
+            }
+        store_pack(reduce_pack(v), k);
+        const i32x4 c2 = reduce_pack(w);
+        if (two) store_pack(c2, k2);
     }
     if (!p.phase_b) return;
 
@@ -326,19 +342,30 @@ __global__ void __launch_bounds__(NT) lamport2_kernel(const Lamport2Params p) {
     const i32x4 armed = {(int)kSent2, (int)kSent2, (int)kSent2, (int)kSent2};
     int64_t spins = 0;
     bool gave_up = false;
+    // The plain loads of the block's next row are issued before the current
+    // row is reduced and written, so they are in flight across its barriers
+    // (a pack that is still armed when loaded goes to the slow pass, as any).
+    auto load_row = [&](int64_t row, i32x4 (&dst)[PPT]) {
+        const uint32_t r2 = row < p.M ? (uint32_t)(row * p.N * 2) : 0u;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+            const int pk = tid + j * NT;
+            const uint32_t off = row < p.M && pk < packs ? r2 + (uint32_t)pk * 16u : kOob;
+            dst[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(st_rs, off, 0, kAuxNontemporal));
+        }
+    };
+    i32x4 qv[PPT];
+    load_row(blockIdx.x, qv);
     for (int64_t row = blockIdx.x; row < p.M; row += gridDim.x) {
         const uint32_t row2 = (uint32_t)(row * p.N * 2);
         auto pack_off = [&](int j) {
             const int pk = tid + j * NT;
             return pk < packs ? row2 + (uint32_t)pk * 16u : kOob;
         };
+        i32x4 qn[PPT];
+        load_row(row + gridDim.x, qn);
         float s[PPT][8];
         uint32_t bad = 0;
-        i32x4 qv[PPT];
-#pragma unroll
-        for (int j = 0; j < PPT; ++j)
-            qv[j] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(st_rs, pack_off(j), 0,
-                                                                                   kAuxNontemporal));
 #pragma unroll
         for (int j = 0; j < PPT; ++j) {
             const uint64_t lo = lo64(qv[j]), hi = hi64(qv[j]);
@@ -401,6 +428,8 @@ __global__ void __launch_bounds__(NT) lamport2_kernel(const Lamport2Params p) {
             __builtin_amdgcn_raw_buffer_store_b128(ov, o_rs, pack_off(j), 0, kAuxNontemporal);
         }
         __syncthreads();  // red[] is rewritten by the next row
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) qv[j] = qn[j];
     }
 }
 

@@ -318,9 +318,23 @@ def gemm_rs_prestaged(A, inputs, torch, iters, warmup, num, M=None, ring=False, 
           if hbm else
           roofline("mfma", flops, st, PEAK_BF16_TFLOPS, "TFLOP/s", traffic,
                    "gemm_rs_ring_kernel" if ring else "gemm_rs_kernel"))
-    return dict(M=M, N=N, K=K, R=R, tile=A.TILE_NAMES[tile], **st, tflops=flops / t / 1e12,
-                frac_mfma=flops / t / 1e12 / PEAK_BF16_TFLOPS, gbs=byts / t / 1e9,
-                frac_hbm=byts / t / 1e9 / PEAK_HBM_GBS, roofline=rf)
+    res = dict(M=M, N=N, K=K, R=R, tile=A.TILE_NAMES[tile], **st, tflops=flops / t / 1e12,
+               frac_mfma=flops / t / 1e12 / PEAK_BF16_TFLOPS, gbs=byts / t / 1e9,
+               frac_hbm=byts / t / 1e9 / PEAK_HBM_GBS, roofline=rf)
+    if not ring:
+        res["library_gemm"] = library_gemm(torch, x, w, iters, warmup)
+    return res
+
+
+def library_gemm(torch, x, w, iters, warmup):
+    """Context only: the plain product X.W of the same shape through
+    torch.matmul (hipBLASLt), no reduce-scatter -- what a library GEMM alone
+    takes on this GPU."""
+    c = torch.empty((x.shape[0], w.shape[1]), dtype=torch.bfloat16, device=x.device)
+    st = time_launches(torch, lambda: torch.matmul(x, w, out=c), iters, warmup)
+    flops = 2.0 * x.shape[0] * x.shape[1] * w.shape[1]
+    return dict(ms_median=st["ms_median"], ms_min=st["ms_min"], tflops=flops / (st["ms_median"] * 1e-3) / 1e12,
+                note="torch.matmul (hipBLASLt) of X.W alone, same shape, no reduce-scatter epilogue")
 
 
 def lamport(A, inputs, torch, iters, warmup, case):
