@@ -474,6 +474,13 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     for (int s0 = 0; s0 < S - 1; ++s0) issue_step(s0);
     wait_oldest_step();
     __syncthreads();
+    // Two-stage ring: step t+1's loads go out right after the barrier that
+    // frees their stage (the one step t-1 used), ahead of the operand reads
+    // and the last MFMAs of step t-1.
+    // (With two stages every wait is vmcnt(0), so steps past the end can be
+    // skipped without upsetting the wait arithmetic.)
+    if constexpr (!kSpreadLoads)
+        if (S - 1 < KT) issue_step(S - 1);
     load_frag(S0, 0, f[0]);
     for (int t = 0; t < KT; ++t) {
         const lds_t *X = S0 + (t % S) * STAGE;
@@ -512,7 +519,6 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
             __syncthreads();
             pieces(S0 + ((t + 1) % S) * STAGE, 0, f[0], f[(NK - 1) & 1], kHalf);
         } else {
-            issue_step(t + S - 1);
 #pragma unroll
             for (int kk = 0; kk + 1 < NK; ++kk) {
                 load_frag(X, kk + 1, f[(kk + 1) & 1]);
@@ -521,6 +527,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
             }
             wait_oldest_step();
             __syncthreads();
+            if (t + S < KT) issue_step(t + S);  // into stage t % S, free since this barrier
             // (after the last step this reads operands that are never used)
             load_frag(S0 + ((t + 1) % S) * STAGE, 0, f[0]);
             mma(f[(NK - 1) & 1]);
