@@ -90,6 +90,11 @@ def lib():
             "arepi_emu_peer_producer": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp,
                                          vp], i32),
             "arepi_emu_producer_gate": ([vp, u32p, i64, vp], i32),
+            "arepi_emu_peer_producer_steps": ([vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, i32, i32, i32, i32,
+                                               i32, vp, vp, i32, u32p, i64, vp], i32),
+            "arepi_emu_signal": ([vp, ctypes.c_uint32, vp], i32),
+            "arepi_emu_stream_create": ([vp], i32),
+            "arepi_emu_stream_destroy": ([vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -354,6 +359,66 @@ def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N:
                                        flag_tile_m, flag_tile_n, scope, workgroups, items_per_release,
                                        _ptr(resident), _stream(stream))
     _check(rc, "emu_peer_producer")
+
+
+def _peer_arrays(src, recv, R, owner, seg, N):
+    sp = (ctypes.c_void_p * R)()
+    rp = (ctypes.c_void_p * R)()
+    for p in range(R):
+        if p == owner:
+            continue
+        _bf16(src[p], "src[%d]" % p, (seg, N))
+        _bf16(recv[p], "recv[%d]" % p, (seg, N))
+        sp[p] = src[p].data_ptr()
+        rp[p] = recv[p].data_ptr()
+    return ctypes.cast(sp, ctypes.c_void_p), ctypes.cast(rp, ctypes.c_void_p)
+
+
+def emu_peer_producer_steps(src, recv, ready_in, orders, R: int, owner: int, M: int, N: int, go, steps: int,
+                            flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT,
+                            workgroups: int = 0, items_per_release: int = 1, resident=None, status=None,
+                            spin_limit: int = 0, stream=None):
+    """Test-only: the emulated peers of `steps` consecutive calls in one launch;
+    step s lands orders[s % len(orders)] once go[0] >= s (raise it with
+    emu_signal after each call).  orders: int32 [n_orders, n_items, 2]."""
+    torch = _torch()
+    _need(orders, "orders", (torch.int32,))
+    if orders.dim() != 3 or orders.shape[2] != 2:
+        raise ValueError("orders must be int32 [n_orders, n_items, 2]")
+    words = gemm_rs_flag_words(M, N, R, flag_tile_m, flag_tile_n)
+    _flags(ready_in, "ready_in", (R, words))
+    _flags(go, "go", (1,))
+    if resident is not None:
+        _flags(resident, "resident", (2,))
+    if status is not None:
+        _flags(status, "status", (1,))
+    sp, rp = _peer_arrays(src, recv, R, owner, M // R, N)
+    rc = lib().arepi_emu_peer_producer_steps(sp, rp, _ptr(ready_in), _ptr(orders), orders.shape[0], orders.shape[1],
+                                             M, N, R, owner, flag_tile_m, flag_tile_n, scope, workgroups,
+                                             items_per_release, _ptr(resident), _ptr(go), steps, _ptr(status),
+                                             spin_limit, _stream(stream))
+    _check(rc, "emu_peer_producer_steps")
+
+
+_emu_streams = {}
+
+
+def emu_stream():
+    """Test-only: a torch stream on a hardware queue of its own (see
+    arepi_emu_stream_create), one per device, kept for the process."""
+    torch = _torch()
+    dev = torch.cuda.current_device()
+    if dev not in _emu_streams:
+        h = ctypes.c_void_p()
+        _check(lib().arepi_emu_stream_create(ctypes.byref(h)), "emu_stream_create")
+        _emu_streams[dev] = torch.cuda.ExternalStream(h.value, device=dev)
+    return _emu_streams[dev]
+
+
+def emu_signal(flag, value: int, stream=None):
+    """Test-only: flag[0] = value once the work queued before it on `stream` has ended."""
+    _flags(flag, "flag", (1,))
+    _check(lib().arepi_emu_signal(_ptr(flag), value, _stream(stream)), "emu_signal")
 
 
 def emu_producer_gate(resident, status=None, spin_limit: int = 0, stream=None):

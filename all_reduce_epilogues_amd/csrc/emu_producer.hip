@@ -9,6 +9,7 @@
 // keeps that cost of the emulation down.
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "arepi_internal.h"
 
@@ -21,24 +22,30 @@ struct EmuParams {
     const uint16_t *src[kMaxR];
     uint16_t *recv[kMaxR];
     uint32_t *ready_in;
-    const int32_t *order;  // [n_items][2] = (peer, tile)
+    const int32_t *order;  // [n_orders][n_items][2] = (peer, tile)
     int64_t n_items, seg, N, ftiles_n, ftiles, fwords;
     int ftm, ftn, R, owner, system_scope;
     int per_release;  // items landed per release
     uint32_t *resident;  // NULL, or [2]: workgroups started, grid size
+    // several steps in one launch: step s uses order s % n_orders and starts
+    // once *go >= s (go NULL: one step, no wait)
+    const uint32_t *go;
+    int steps, n_orders;
+    uint32_t *status;
+    int64_t spin_limit;
 };
 
-__device__ bool item_valid(const EmuParams &p, const int64_t item, int &peer, int64_t &t) {
-    peer = p.order[2 * item];
-    t = p.order[2 * item + 1];
+__device__ bool item_valid(const EmuParams &p, const int32_t *order, const int64_t item, int &peer, int64_t &t) {
+    peer = order[2 * item];
+    t = order[2 * item + 1];
     return peer >= 0 && peer < p.R && peer != p.owner && t >= 0 && t < p.ftiles;
 }
 
 // Copies one (peer, flag tile) item with the whole workgroup (no drain).
-__device__ void copy_item(const EmuParams &p, const int64_t item) {
+__device__ void copy_item(const EmuParams &p, const int32_t *order, const int64_t item) {
     int peer;
     int64_t t;
-    if (!item_valid(p, item, peer, t)) return;  // uniform across the workgroup
+    if (!item_valid(p, order, item, peer, t)) return;  // uniform across the workgroup
     const int64_t r0 = (t / p.ftiles_n) * p.ftm, c0 = (t % p.ftiles_n) * p.ftn;
     const int64_t rows = min((int64_t)p.ftm, p.seg - r0);
     const int64_t packs = min((int64_t)p.ftn, p.N - c0) / 8;
@@ -91,23 +98,50 @@ __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
         __hip_atomic_store(p.resident + 1, gridDim.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_add(p.resident, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    __shared__ int stop;
     const int64_t K = p.per_release, batches = (p.n_items + K - 1) / K;
-    for (int64_t j = blockIdx.x; j < batches; j += gridDim.x) {
-        const int64_t i0 = j * K, i1 = min(i0 + K, p.n_items);
-        for (int64_t item = i0; item < i1; ++item) copy_item(p, item);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const bool sys = p.system_scope != 0;
-            fence_release(sys);
-            for (int64_t item = i0; item < i1; ++item) {
-                int peer;
-                int64_t t;
-                if (item_valid(p, item, peer, t))
-                    fetch_or_relaxed(p.ready_in + (int64_t)peer * p.fwords + (t >> 5), 1u << (t & 31), sys);
+    const bool sys = p.system_scope != 0;
+    for (int st = 0; st < p.steps; ++st) {
+        if (p.go) {
+            // wait for the consumer of step st-1 to be done with recv and ready_in
+            if (threadIdx.x == 0) {
+                int64_t n = 0;
+                const uint64_t t0 = spin_clock();
+                stop = 0;
+                while (load_relaxed(p.go, false) < (uint32_t)st) {
+                    if (spin_expired(p.spin_limit, n, t0)) {
+                        stop = 1;
+                        if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(2);
+                }
+            }
+            __syncthreads();
+            if (stop) return;
+        }
+        const int32_t *order = p.order + (int64_t)(st % p.n_orders) * p.n_items * 2;
+        for (int64_t j = blockIdx.x; j < batches; j += gridDim.x) {
+            const int64_t i0 = j * K, i1 = min(i0 + K, p.n_items);
+            for (int64_t item = i0; item < i1; ++item) copy_item(p, order, item);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                fence_release(sys);
+                for (int64_t item = i0; item < i1; ++item) {
+                    int peer;
+                    int64_t t;
+                    if (item_valid(p, order, item, peer, t))
+                        fetch_or_relaxed(p.ready_in + (int64_t)peer * p.fwords + (t >> 5), 1u << (t & 31), sys);
+                }
             }
         }
     }
+}
+
+// One thread: *flag = value after everything before it on the stream.
+__global__ void emu_signal_kernel(uint32_t *flag, uint32_t value) {
+    __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One wave, launched on the consumer's stream between the producer and the
@@ -141,12 +175,12 @@ __global__ void __launch_bounds__(64) emu_gate_kernel(uint32_t *resident, uint32
 
 using namespace arepi;
 
-extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
-                                       const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
-                                       int owner, int flag_tile_m, int flag_tile_n, int scope,
-                                       int workgroups, int items_per_release, uint32_t *resident,
-                                       arepi_stream_t stream) {
-    auto bad = [](const std::string &m) { return fail(AREPI_EINVAL, "arepi_emu_peer_producer: " + m); };
+static int emu_launch(const char *who, const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
+                      const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R, int owner,
+                      int flag_tile_m, int flag_tile_n, int scope, int workgroups, int items_per_release,
+                      uint32_t *resident, const uint32_t *go, int steps, int n_orders, uint32_t *status,
+                      int64_t spin_limit, arepi_stream_t stream) {
+    auto bad = [who](const std::string &m) { return fail(AREPI_EINVAL, std::string(who) + ": " + m); };
     if (R < 1 || R > kMaxR) return bad("R=" + std::to_string(R) + " outside [1, 8]");
     if (owner < 0 || owner >= R) return bad("owner outside [0, R-1]");
     if (M < 1 || M % R) return bad("M must be a positive multiple of R");
@@ -157,6 +191,7 @@ extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *con
     if (n_items < 0 || n_items > (int64_t)1 << 30) return bad("n_items out of range");
     if (workgroups < 0) return bad("workgroups must be >= 0 (0: one per batch)");
     if (items_per_release < 1) return bad("items_per_release must be >= 1");
+    if (steps < 1 || n_orders < 1) return bad("steps and n_orders must be >= 1");
     if (n_items == 0) return ok();
     if (!src || !recv || !ready_in || !order) return bad("src, recv, ready_in and order must be non-NULL");
     EmuParams p{};
@@ -182,11 +217,46 @@ extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *con
     p.system_scope = scope == AREPI_SCOPE_SYSTEM ? 1 : 0;
     p.per_release = items_per_release;
     p.resident = resident;
+    p.go = go;
+    p.steps = steps;
+    p.n_orders = n_orders;
+    p.status = status;
+    p.spin_limit = spin_bound(spin_limit);
     const int64_t batches = (n_items + items_per_release - 1) / items_per_release;
     const int64_t groups = workgroups == 0 ? batches : std::min<int64_t>(workgroups, batches);
     hipLaunchKernelGGL(emu_producer_kernel, dim3((unsigned)groups), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), p);
-    return check_launch("arepi_emu_peer_producer");
+    return check_launch(who);
+}
+
+extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
+                                       const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R,
+                                       int owner, int flag_tile_m, int flag_tile_n, int scope,
+                                       int workgroups, int items_per_release, uint32_t *resident,
+                                       arepi_stream_t stream) {
+    return emu_launch("arepi_emu_peer_producer", src, recv, ready_in, order, n_items, M, N, R, owner,
+                      flag_tile_m, flag_tile_n, scope, workgroups, items_per_release, resident, nullptr, 1, 1,
+                      nullptr, 0, stream);
+}
+
+extern "C" int arepi_emu_peer_producer_steps(const uint16_t *const *src, uint16_t *const *recv,
+                                             uint32_t *ready_in, const int32_t *orders, int n_orders,
+                                             int64_t n_items, int64_t M, int64_t N, int R, int owner,
+                                             int flag_tile_m, int flag_tile_n, int scope, int workgroups,
+                                             int items_per_release, uint32_t *resident, const uint32_t *go,
+                                             int steps, uint32_t *status, int64_t spin_limit,
+                                             arepi_stream_t stream) {
+    if (!go) return fail(AREPI_EINVAL, "arepi_emu_peer_producer_steps: go must be non-NULL");
+    return emu_launch("arepi_emu_peer_producer_steps", src, recv, ready_in, orders, n_items, M, N, R, owner,
+                      flag_tile_m, flag_tile_n, scope, workgroups, items_per_release, resident, go, steps,
+                      n_orders, status, spin_limit, stream);
+}
+
+extern "C" int arepi_emu_signal(uint32_t *flag, uint32_t value, arepi_stream_t stream) {
+    if (!flag) return fail(AREPI_EINVAL, "arepi_emu_signal: flag must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(flag) & 3u) return fail(AREPI_EINVAL, "arepi_emu_signal: flag must be 4-byte aligned");
+    hipLaunchKernelGGL(emu_signal_kernel, dim3(1), dim3(1), 0, reinterpret_cast<hipStream_t>(stream), flag, value);
+    return check_launch("arepi_emu_signal");
 }
 
 extern "C" int arepi_emu_producer_gate(uint32_t *resident, uint32_t *status, int64_t spin_limit,
@@ -197,4 +267,29 @@ extern "C" int arepi_emu_producer_gate(uint32_t *resident, uint32_t *status, int
     hipLaunchKernelGGL(emu_gate_kernel, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), resident,
                        status, spin_bound(spin_limit));
     return check_launch("arepi_emu_producer_gate");
+}
+
+extern "C" int arepi_emu_stream_create(arepi_stream_t *stream) {
+    if (!stream) return fail(AREPI_EINVAL, "arepi_emu_stream_create: stream must be non-NULL");
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return fail(AREPI_ELAUNCH, "arepi_emu_stream_create: device query failed");
+    // every compute unit enabled: the mask only buys the queue of its own
+    std::vector<uint32_t> mask((cus + 31) / 32, 0u);
+    for (int c = 0; c < cus; ++c) mask[c / 32] |= 1u << (c % 32);
+    hipStream_t s = nullptr;
+    const hipError_t e = hipExtStreamCreateWithCUMask(&s, (uint32_t)mask.size(), mask.data());
+    if (e != hipSuccess)
+        return fail(AREPI_ELAUNCH, std::string("arepi_emu_stream_create: ") + hipGetErrorString(e));
+    *stream = reinterpret_cast<arepi_stream_t>(s);
+    return ok();
+}
+
+extern "C" int arepi_emu_stream_destroy(arepi_stream_t stream) {
+    if (!stream) return fail(AREPI_EINVAL, "arepi_emu_stream_destroy: stream must be non-NULL");
+    const hipError_t e = hipStreamDestroy(reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(AREPI_ELAUNCH, std::string("arepi_emu_stream_destroy: ") + hipGetErrorString(e));
+    return ok();
 }

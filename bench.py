@@ -5,8 +5,9 @@ the tp=4 share -- X [4096,2048] . W [2048,4096] bf16, R=4, owner segment of 1024
 rows, three peer partials landed per 128x128 flag tile by an emulated-peer
 producer on a second stream in shuffled order, their ready bits published
 eight tiles per release -- as TFLOP/s of the whole step (2*M*N*K per step).
-Each step queues the producer, then a one-wave gate on the GEMM's stream
-that waits until every producer workgroup has started, then the GEMM.
+One producer launch serves all the steps: a one-wave gate on the GEMM's
+stream waits until every producer workgroup has started, then the GEMMs run
+back to back, each step's tiles landing once the previous GEMM has ended.
 The same step with one release per tile is reported beside it in `config`.
 Inputs are resident in HBM before timing starts.
 
@@ -64,16 +65,26 @@ PRODUCER_WORKGROUPS = 96
 LEGS = ("gemm_rs", "gemm_rs_tiny", "gemm_rs_prestaged", "gemm_rs_tp8", "lamport", "combine", "combine_lds",
         "lamport_2phase", "gemm_rs_fp8", "gemm_rs_ring", "gemm_rs_ring_prestaged")
 
-_side_stream = None
-
-
 def side_stream(torch):
-    """One second stream for every leg: streams share a few hardware queues,
-    and a fresh stream per leg can land on the main stream's queue."""
-    global _side_stream
-    if _side_stream is None:
-        _side_stream = torch.cuda.Stream()
-    return _side_stream
+    """The second stream of every leg: one with a hardware queue of its own
+    (ordinary streams share a few hardware queues, and one that shared the
+    main stream's queue would run the emulated peers in series with the GEMM
+    instead of beside it).  It is a blocking stream: work on the legacy
+    default stream waits for it."""
+    import all_reduce_epilogues_amd as A
+    return A.emu_stream()
+
+
+_main_stream = None
+
+
+def main_stream(torch):
+    """A non-blocking stream for the consumer of the legs whose producer
+    runs beside it (the legacy default stream would wait for the producer)."""
+    global _main_stream
+    if _main_stream is None:
+        _main_stream = torch.cuda.Stream()
+    return _main_stream
 
 
 class _HipEvents:
@@ -191,21 +202,22 @@ def _ready_all(torch, R, absent, words, tiles):
 
 def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs=PRODUCER_WORKGROUPS,
                        per_release=1):
-    """tp=4 share; a producer stream lands the peers while the GEMM runs
-    (ring=True: the push-ring hop, the producer landing the upstream partials).
+    """tp=4 share; a producer lands the peers while the GEMM runs (ring=True:
+    the push-ring hop, the producer landing the upstream partials).
 
-    The main stream runs only the GEMMs, back to back.  Each consumes its
-    ready_in bits (the owner tiles clear what they waited for), so ready_in is
-    zero again when it ends and needs no clearing kernel.  The producer of step
-    i, on the side stream, waits for GEMM i-1 to end (it reuses recv and
-    ready_in) and then runs while GEMM i does; GEMM i's owner tiles wait for
-    its bits.  Between the two GEMMs the main stream holds a one-wave gate
-    that returns once every producer workgroup of step i has started, so GEMM
-    i cannot take the compute units the producer needs.  ready_out is only
-    ever OR-ed into.
+    One producer launch on the side stream serves all the steps of a phase
+    (warm-up, then the timed steps): it is resident before the first GEMM (the
+    one-wave gate on the main stream waits for all its workgroups to start),
+    and step i's tiles start landing once the main stream has signalled that
+    GEMM i-1 has ended (it reuses recv and ready_in); they land while GEMM i
+    runs, whose owner tiles wait for their bits.  The main stream runs the
+    GEMMs back to back with a one-thread signal kernel between them.  Each GEMM
+    consumes its ready_in bits (the owner tiles clear what they waited for), so
+    ready_in is zero again when it ends.  ready_out is only ever OR-ed into.
 
-    Returns the wall time per step and the GEMM's average launch duration from
-    HIP events recorded on its stream just before and after each launch.
+    Returns the wall time per step (the one producer launch and gate of the
+    phase included) and the GEMM's launch durations from HIP events recorded
+    on its stream just before and after each launch.
     """
     dev = torch.device("cuda:0")
     if ring:  # push-ring hop: upstream partials of every segment but the chain one
@@ -223,42 +235,47 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
     recv = [None if p == absent else torch.zeros_like(src[p]) for p in range(R)]
     words = A.gemm_rs_flag_words(M, N, R)
     tiles = ((seg + 127) // 128) * ((N + 127) // 128)
-    orders = [torch.from_numpy(inputs.producer_order(R, absent, tiles, 2000 + i)).to(dev) for i in range(4)]
+    import numpy as np
+    orders = torch.from_numpy(np.stack([inputs.producer_order(R, absent, tiles, 2000 + i) for i in range(4)])).to(dev)
     rin = torch.zeros((R, words), dtype=torch.int32, device=dev)
     rout = torch.zeros((R, words), dtype=torch.int32, device=dev)
     out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
     send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     resident = torch.zeros(2, dtype=torch.int32, device=dev)
-    main = torch.cuda.current_stream()
+    go = torch.zeros(1, dtype=torch.int32, device=dev)
+    main = main_stream(torch)
     side = side_stream(torch)
+    torch.cuda.synchronize()
     tile = (A.gemm_rs_ring_pick_tile if ring else A.gemm_rs_pick_tile)(M, N, K, R, owner, publish=True)
     n_ev = steps + warmup
     H = _HipEvents()
     ev_gs = [H.create() for _ in range(n_ev)]
     ev_ge = [H.create() for _ in range(n_ev)]
 
-    def step(i):
-        if i > 0:
-            H.wait(side, ev_ge[i - 1])
-        A.emu_peer_producer(src, recv, rin, orders[i % len(orders)], R, absent, M, N, workgroups=producer_wgs,
-                            items_per_release=per_release, resident=resident, stream=side)
+    def phase(first, n):
+        with torch.cuda.stream(main):
+            go.zero_()
+        side.wait_stream(main)
+        A.emu_peer_producer_steps(src, recv, rin, orders, R, absent, M, N, go, n, workgroups=producer_wgs,
+                                  items_per_release=per_release, resident=resident, status=status, stream=side)
         A.emu_producer_gate(resident, status=status, stream=main)
-        H.record(ev_gs[i], main)
-        if ring:
-            A.gemm_rs_ring(x, w, recv, rin, out, send, R, owner, ready_out=rout,
-                           tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
-        else:
-            A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout,
-                            tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
-        H.record(ev_ge[i], main)
+        for s in range(n):
+            i = first + s
+            H.record(ev_gs[i], main)
+            if ring:
+                A.gemm_rs_ring(x, w, recv, rin, out, send, R, owner, ready_out=rout,
+                               tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
+            else:
+                A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout,
+                                tile=tile | A.TILE_CONSUME_READY, status=status, stream=main)
+            H.record(ev_ge[i], main)
+            A.emu_signal(go, s + 1, stream=main)
 
-    for i in range(warmup):
-        step(i)
+    phase(0, warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(warmup, warmup + steps):
-        step(i)
+    phase(warmup, steps)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     gemm = stats([H.elapsed_ms(ev_gs[i], ev_ge[i]) for i in range(warmup, warmup + steps)])
@@ -633,7 +650,7 @@ def main():
         "config": {"workload": "gemm_rs tp4 share: X[4096,2048] x W[2048,4096] bf16, R=4, owner=0, "
                                "3 peer partials [1024,4096] landed per 128x128 flag tile by a producer "
                                "stream (96 workgroups) in shuffled order, their bits published 8 tiles per "
-                               "release; a gate holds the GEMM until every producer workgroup has started; "
+                               "release; one producer launch serves every step, resident before the first GEMM; "
                                "send + ready_out published",
                    "M": 4096, "N": 4096, "K": 2048, "R": 4, "owner": 0,
                    "producer_tiles_per_release": PRODUCER_TILES_PER_RELEASE,

@@ -375,6 +375,38 @@ int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, u
                             int owner, int flag_tile_m, int flag_tile_n, int scope, int workgroups,
                             int items_per_release, uint32_t *resident, arepi_stream_t stream);
 
+/* Test-only: the emulated peers of `steps` consecutive consumer calls in one
+ * launch, so that the producer is resident once for all of them.  Step s
+ * lands the n_items items of orders[s % n_orders] (device int32
+ * [n_orders][n_items][2]) exactly as arepi_emu_peer_producer does, after
+ * waiting until *go >= s (device uint32, 0 before the launch; the consumer's
+ * stream raises it with arepi_emu_signal(go, s, ...) once the consumer of
+ * step s-1 has ended and no longer reads recv or ready_in).  That consumer
+ * needs nothing from step s, so every wait ends; each is bounded by
+ * spin_limit (encoding above), and on expiry the producer ORs
+ * AREPI_STATUS_TIMEOUT into *status (status may be NULL) and stops.  Issue it
+ * with `resident` and arepi_emu_producer_gate before the first consumer.
+ * Errors: those of arepi_emu_peer_producer, plus go NULL, steps < 1 or
+ * n_orders < 1. */
+int arepi_emu_peer_producer_steps(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
+                                  const int32_t *orders, int n_orders, int64_t n_items, int64_t M, int64_t N,
+                                  int R, int owner, int flag_tile_m, int flag_tile_n, int scope, int workgroups,
+                                  int items_per_release, uint32_t *resident, const uint32_t *go, int steps,
+                                  uint32_t *status, int64_t spin_limit, arepi_stream_t stream);
+
+/* Test-only: a stream with a hardware queue of its own, for the emulated
+ * producer.  The HIP runtime hands ordinary streams out of a small pool of
+ * hardware queues, so two of them may share one, and a queue runs its
+ * kernels in order; a stream created with a compute-unit mask gets a queue
+ * that is never pooled.  The mask here enables every compute unit.  Default
+ * priority.  Destroy with arepi_emu_stream_destroy. */
+int arepi_emu_stream_create(arepi_stream_t *stream);
+int arepi_emu_stream_destroy(arepi_stream_t stream);
+
+/* Test-only: one thread stores `value` into *flag (device uint32, relaxed,
+ * agent scope) once everything issued before it on `stream` has ended. */
+int arepi_emu_signal(uint32_t *flag, uint32_t value, arepi_stream_t stream);
+
 /* Test-only forward-progress gate for a consumer that waits on the emulated
  * producer on the same GPU (the aiter PR #4977 Correctness notes: producer
  * work must not be left unscheduled behind spinning consumers).  Launch it on

@@ -207,6 +207,10 @@ def test_lamport_and_combine_validate_before_launch():
     assert "items_per_release" in A.last_error()
     assert L.arepi_emu_producer_gate(None, None, 0, None) == A.EINVAL
     assert "resident" in A.last_error()
+    assert L.arepi_emu_peer_producer_steps(None, None, None, None, 1, 1, 256, 512, 2, 0, 128, 128, 0, 0, 1,
+                                           None, None, 2, None, 0, None) == A.EINVAL
+    assert "go" in A.last_error()
+    assert L.arepi_emu_signal(None, 1, None) == A.EINVAL
 
 
 def test_noalloc_consumer_refuses_sizes_beyond_its_static_staging():

@@ -248,6 +248,49 @@ def test_gate_lets_the_producer_finish_beside_a_register_full_gemm():
         assert not resident.any().item(), "the gate must leave resident at zero"
 
 
+def test_one_producer_launch_feeds_consecutive_calls():
+    """One multi-step producer launch, on a stream with a hardware queue of its
+    own, lands the peers of four consecutive GEMM-RS calls (step s once the
+    call before has signalled its end); each call consumes its bits.  Every
+    call equals the pre-staged result, and ready_in and resident end zero."""
+    case = inputs.workload_gemm_rs(2)
+    M, N, R, owner = case["M"], case["N"], case["R"], case["owner"]
+    seg = M // R
+    dev = device()
+    pre = run(case)
+    tiles = oracle.flag_tiles(M, N, R, 128, 128)
+    orders = torch.from_numpy(np.stack([inputs.producer_order(R, owner, tiles, 40 + i) for i in range(3)])).to(dev)
+    x, w = to_dev_bf16(case["x"]), to_dev_bf16(case["w"])
+    src = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
+    recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
+    rin = torch.zeros((R, A.gemm_rs_flag_words(M, N, R)), dtype=torch.int32, device=dev)
+    rout = torch.zeros_like(rin)
+    send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    outs = [torch.empty((seg, N), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    go = torch.zeros(1, dtype=torch.int32, device=dev)
+    resident = torch.zeros(2, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    # the producer's stream synchronises with the legacy default stream (it is
+    # a blocking stream), so the consumer runs on a non-blocking one
+    side = A.emu_stream()
+    main = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print("multi-step producer, 4 steps", flush=True)
+    A.emu_peer_producer_steps(src, recv, rin, orders, R, owner, M, N, go, 4, workgroups=96, items_per_release=8,
+                              resident=resident, status=status, stream=side)
+    A.emu_producer_gate(resident, status=status, stream=main)
+    for s in range(4):
+        A.gemm_rs_fused(x, w, recv, rin, outs[s], R, owner, send=send, ready_out=rout,
+                        tile=A.TILE_CONSUME_READY, status=status, stream=main)
+        A.emu_signal(go, s + 1, stream=main)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "a wait timed out"
+    for s in range(4):
+        assert np.array_equal(from_dev_bf16(outs[s]), pre["out"]), "call %d" % s
+    assert not rin.any().item() and not resident.any().item()
+    assert int(go.item()) == 4
+
+
 def test_gate_times_out_when_no_producer_announces():
     """Nothing ever starts on `resident`: the gate's bounded wait gives up,
     reports the time-out and finishes."""
