@@ -403,6 +403,20 @@ def emu_peer_producer_steps(src, recv, ready_in, orders, R: int, owner: int, M: 
 _emu_streams = {}
 
 
+def _destroy_emu_streams():
+    """At exit: finish and destroy the streams emu_stream() created."""
+    if not _emu_streams:
+        return
+    torch = _torch()
+    for dev, st in list(_emu_streams.items()):
+        try:
+            st.synchronize()
+            lib().arepi_emu_stream_destroy(ctypes.c_void_p(st.cuda_stream))
+        except Exception:
+            pass
+    _emu_streams.clear()
+
+
 def emu_stream():
     """Test-only: a torch stream on a hardware queue of its own (see
     arepi_emu_stream_create), one per device, kept for the process."""
@@ -411,6 +425,9 @@ def emu_stream():
     if dev not in _emu_streams:
         h = ctypes.c_void_p()
         _check(lib().arepi_emu_stream_create(ctypes.byref(h)), "emu_stream_create")
+        if not _emu_streams:
+            import atexit
+            atexit.register(_destroy_emu_streams)
         _emu_streams[dev] = torch.cuda.ExternalStream(h.value, device=dev)
     return _emu_streams[dev]
 

@@ -408,7 +408,8 @@ def gemm_rs_fp8_prestaged(A, inputs, torch, iters, warmup):
     return dict(M=M, N=N, K=K, R=R, tile="256x256", **st, tflops=flops / t / 1e12,
                 frac_mfma_fp8=flops / t / 1e12 / PEAK_FP8_TFLOPS, gbs=byts / t / 1e9,
                 frac_hbm=byts / t / 1e9 / PEAK_HBM_GBS,
-                roofline=roofline("mfma", flops, st, PEAK_FP8_TFLOPS, "TFLOP/s", None, "gemm_rs_kernel (fp8)"))
+                roofline=roofline("mfma", flops, st, PEAK_FP8_TFLOPS, "TFLOP/s",
+                                  measured_traffic("gemm_rs_fp8", "256x256"), "gemm_rs_fp8_kernel"))
 
 
 def lamport_2phase(A, inputs, torch, iters, warmup, case):
@@ -525,6 +526,7 @@ COUNTERS = {
     "combine": ("combine_counters.txt", ("combine.hip",)),
     "combine_lds": ("combine_counters_lds.txt", ("combine.hip",)),
     "lamport_2phase": ("lamport_2phase_counters.txt", ("lamport.hip",)),
+    "gemm_rs_fp8": ("gemm_rs_fp8_tp4_counters.txt", ("gemm_rs_impl.h", "gemm_rs_fp8.hip")),
 }
 COUNTERS_FILE = None   # (tests) one record file used for every key instead
 
