@@ -65,12 +65,26 @@ PRODUCER_WORKGROUPS = 96
 LEGS = ("gemm_rs", "gemm_rs_tiny", "gemm_rs_prestaged", "gemm_rs_tp8", "lamport", "combine", "combine_lds",
         "lamport_2phase", "gemm_rs_fp8", "gemm_rs_ring", "gemm_rs_ring_prestaged")
 
+_side_stream = None
+
+
 def side_stream(torch):
-    """The second stream of every leg: one with a hardware queue of its own
-    (ordinary streams share a few hardware queues, and one that shared the
-    main stream's queue would run the emulated peers in series with the GEMM
-    instead of beside it).  It is a blocking stream: work on the legacy
-    default stream waits for it."""
+    """The second stream of the legs whose emulated peers run before each
+    timed call (Lamport, two-phase): an ordinary non-blocking stream, created
+    once (streams share a few hardware queues, and a fresh one per leg can
+    land on the main stream's queue)."""
+    global _side_stream
+    if _side_stream is None:
+        _side_stream = torch.cuda.Stream()
+    return _side_stream
+
+
+def producer_stream(torch):
+    """The stream of the producer that runs beside the GEMM: one with a
+    hardware queue of its own (a producer that waits for the GEMM's signal
+    must never sit in front of that GEMM in a shared queue).  It is a blocking
+    stream, which the legacy default stream waits for, so those legs run
+    their GEMMs on main_stream()."""
     import all_reduce_epilogues_amd as A
     return A.emu_stream()
 
@@ -245,7 +259,7 @@ def gemm_rs_concurrent(A, inputs, torch, steps, warmup, ring=False, producer_wgs
     resident = torch.zeros(2, dtype=torch.int32, device=dev)
     go = torch.zeros(1, dtype=torch.int32, device=dev)
     main = main_stream(torch)
-    side = side_stream(torch)
+    side = producer_stream(torch)
     torch.cuda.synchronize()
     tile = (A.gemm_rs_ring_pick_tile if ring else A.gemm_rs_pick_tile)(M, N, K, R, owner, publish=True)
     n_ev = steps + warmup
