@@ -291,6 +291,30 @@ def test_one_producer_launch_feeds_consecutive_calls():
     assert int(go.item()) == 4
 
 
+def test_multi_step_producer_gives_up_when_no_signal_comes():
+    """Step 0 lands at once; step 1 waits for a signal the host never sends:
+    the producer's bounded wait gives up, reports the time-out and the kernel
+    finishes, with step 0's bits set."""
+    case = inputs.workload_gemm_rs(1)
+    M, N, R, owner = case["M"], case["N"], case["R"], case["owner"]
+    dev = device()
+    tiles = oracle.flag_tiles(M, N, R, 128, 128)
+    orders = torch.from_numpy(np.stack([inputs.producer_order(R, owner, tiles, 50)])).to(dev)
+    src = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
+    recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
+    rin = torch.zeros((R, A.gemm_rs_flag_words(M, N, R)), dtype=torch.int32, device=dev)
+    go = torch.zeros(1, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    A.emu_peer_producer_steps(src, recv, rin, orders, R, owner, M, N, go, 2, status=status, spin_limit=2000,
+                              stream=A.emu_stream())
+    torch.cuda.synchronize()
+    assert int(status.item()) & A.STATUS_TIMEOUT
+    assert np.array_equal(from_dev_u32(rin), flag_words_all_set(R, owner, tiles))
+    for p in range(R):
+        if p != owner:
+            assert torch.equal(recv[p], src[p])
+
+
 def test_gate_times_out_when_no_producer_announces():
     """Nothing ever starts on `resident`: the gate's bounded wait gives up,
     reports the time-out and finishes."""

@@ -271,6 +271,46 @@ def test_consume_ready_leaves_ready_in_clear():
         check(case, res, what="ring consume call %d" % call, ref=ref)
 
 
+def test_one_producer_launch_feeds_consecutive_hops():
+    """The push-ring hop fed by one multi-step producer launch (on a stream
+    with a hardware queue of its own) over three consecutive calls, each
+    consuming its bits: every call equals the pre-staged hop."""
+    R, owner = 4, 1
+    M, N, K = 1024, 1024, 512
+    case = inputs.gemm_rs_ring_case(M, N, K, R, owner=owner, seed=88)
+    chain = (owner + R - 1) % R
+    dev = device()
+    tile = A.TILE_256x256_W8_K64
+    pre = run(case, tile=tile, publish=False)
+    seg = M // R
+    tiles = oracle.flag_tiles(M, N, R, 128, 128)
+    orders = torch.from_numpy(np.stack([inputs.producer_order(R, chain, tiles, 60 + i) for i in range(2)])).to(dev)
+    x, w = to_dev_bf16(case["x"]), to_dev_bf16(case["w"])
+    src = [None if p == chain else to_dev_bf16(case["up"][p]) for p in range(R)]
+    up = [None if p == chain else torch.zeros_like(src[p]) for p in range(R)]
+    rin = torch.zeros((R, A.gemm_rs_flag_words(M, N, R)), dtype=torch.int32, device=dev)
+    go = torch.zeros(1, dtype=torch.int32, device=dev)
+    resident = torch.zeros(2, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    outs = [torch.empty((seg, N), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    main = torch.cuda.Stream()  # the producer's stream is a blocking one
+    torch.cuda.synchronize()
+    print("ring hop, multi-step producer", flush=True)
+    A.emu_peer_producer_steps(src, up, rin, orders, R, chain, M, N, go, 3, workgroups=16, items_per_release=4,
+                              resident=resident, status=status, stream=A.emu_stream())
+    A.emu_producer_gate(resident, status=status, stream=main)
+    for s in range(3):
+        A.gemm_rs_ring(x, w, up, rin, outs[s], send, R, owner, tile=tile | A.TILE_CONSUME_READY, status=status,
+                       stream=main)
+        A.emu_signal(go, s + 1, stream=main)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "a wait timed out"
+    for s in range(3):
+        assert np.array_equal(from_dev_bf16(outs[s]), pre["out"]), "call %d" % s
+    assert not rin.any().item()
+
+
 def test_timeout_reports_status_and_finishes():
     M, N, K, R, owner = 256, 512, 256, 2, 0
     case = inputs.gemm_rs_ring_case(M, N, K, R, owner=owner, seed=5)
