@@ -29,6 +29,7 @@ STATUS_TIMEOUT = 1
  TILE_256x128_S3, TILE_128x256_S3, TILE_128x128_S4, TILE_256x256_W8, TILE_256x256_W8_K64) = range(12)
 TILE_PAIRED_ROWS = 0x200  # OR into an explicit tile: pair owner half-blocks with non-owner ones
 TILE_CONSUME_READY = 0x400  # OR into any tile: owner tiles clear the ready_in bits they waited for
+TILE_OWNER_FIRST = 0x800  # OR into a contiguous tile: the owner's row blocks first (partials already landed)
 LAMPORT_NOALLOC_BYTES = 32 * 1024 * 1024  # static staging of ar_rmsnorm_lamport_noalloc
 TILE_NAMES = {TILE_256x256: "256x256", TILE_128x256: "128x256", TILE_128x128: "128x128",
               TILE_64x128: "64x128", TILE_32x256: "32x256", TILE_256x256_S4: "256x256_s4",

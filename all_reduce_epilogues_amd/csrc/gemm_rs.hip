@@ -39,6 +39,9 @@ extern "C" int arepi_gemm_rs_supports(int64_t M, int64_t N, int64_t K, int R, in
                                       int flag_tile_m, int flag_tile_n, int publish, int tile_cfg) {
     int rc = validate_shape(M, N, K, R, owner, flag_tile_m, flag_tile_n);
     if (rc) return rc;
+    if ((tile_cfg & AREPI_TILE_OWNER_FIRST) && (tile_cfg & AREPI_TILE_PAIRED_ROWS))
+        return fail(AREPI_EINVAL, "arepi_gemm_rs: AREPI_TILE_OWNER_FIRST needs the contiguous row layout");
+    tile_cfg &= ~AREPI_TILE_OWNER_FIRST;
     const bool consume = (tile_cfg & AREPI_TILE_CONSUME_READY) != 0;
     // consuming readiness bits needs the same nesting as publishing them
     const bool nest = publish || consume;
@@ -99,7 +102,7 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
     p.spin_limit = spin_bound(spin_limit);
     p.system_scope = scope == AREPI_SCOPE_SYSTEM;
     p.consume = c.consume ? 1 : 0;
-    rc = plan(p, c.t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous);
+    rc = plan(p, c.t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous, c.owner_first);
     if (rc) return rc;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -121,7 +124,7 @@ extern "C" int64_t arepi_gemm_rs_schedule(int64_t M, int64_t N, int64_t K, int R
     const CfgChoice c = decode_cfg(M, N, K, R, flag_tile_m, flag_tile_n, publish != 0, tile_cfg);
     const TileCfg *t = c.t;
     GemmRsParams p{};
-    rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous);
+    rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous, c.owner_first);
     if (rc) return rc;
     if (rows) {
         if (capacity < (int64_t)p.nWG * 6)

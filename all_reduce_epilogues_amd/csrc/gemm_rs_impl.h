@@ -1229,7 +1229,7 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool pub
 
 // Launch geometry (everything but the pointers) for tile t.
 int plan(GemmRsParams &p, const TileCfg *t, int64_t M, int64_t N, int64_t K, int R, int owner, int ftm, int ftn,
-         bool publish, bool contiguous) {
+         bool publish, bool contiguous, bool owner_first = false) {
     p.M = M;
     p.N = N;
     p.K = K;
@@ -1252,8 +1252,11 @@ int plan(GemmRsParams &p, const TileCfg *t, int64_t M, int64_t N, int64_t K, int
         p.ob1 = 0;
     } else {
         p.nRB = (int)cdiv(M, t->BM);
-        // first row block after the owner's: the rotation puts the owner's last
-        p.ob1 = (int)(cdiv((int64_t)(owner + 1) * p.seg, t->BM) % p.nRB);
+        // first row block after the owner's: the rotation puts the owner's
+        // last; or (owner_first) the owner's first row block, which puts them
+        // first
+        p.ob1 = owner_first ? (int)(((int64_t)owner * p.seg / t->BM) % p.nRB)
+                            : (int)(cdiv((int64_t)(owner + 1) * p.seg, t->BM) % p.nRB);
     }
     p.group = 4;
     p.xcd_chunk = 32;
@@ -1267,7 +1270,7 @@ int plan(GemmRsParams &p, const TileCfg *t, int64_t M, int64_t N, int64_t K, int
 struct CfgChoice {
     const TileCfg *t;
     int id;
-    bool contiguous, consume, nest;
+    bool contiguous, consume, nest, owner_first;
 };
 CfgChoice decode_cfg(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool publish, int tile_cfg,
                      bool whole_segments = false) {
@@ -1275,7 +1278,8 @@ CfgChoice decode_cfg(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, b
     c.consume = (tile_cfg & AREPI_TILE_CONSUME_READY) != 0;
     c.nest = publish || c.consume;
     c.contiguous = (tile_cfg & AREPI_TILE_PAIRED_ROWS) == 0;
-    const int id = tile_cfg & ~(AREPI_TILE_PAIRED_ROWS | AREPI_TILE_CONSUME_READY);
+    c.owner_first = (tile_cfg & AREPI_TILE_OWNER_FIRST) != 0;
+    const int id = tile_cfg & ~(AREPI_TILE_PAIRED_ROWS | AREPI_TILE_CONSUME_READY | AREPI_TILE_OWNER_FIRST);
     c.id = id == AREPI_TILE_AUTO ? pick_tile(M, N, K, R, ftm, ftn, c.nest, whole_segments && publish) : id;
     c.t = find_tile(c.id);
     return c;

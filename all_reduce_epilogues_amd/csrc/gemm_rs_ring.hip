@@ -67,6 +67,8 @@ extern "C" int arepi_gemm_rs_ring_supports(int64_t M, int64_t N, int64_t K, int 
                                            int flag_tile_n, int publish, int tile_cfg) {
     if (tile_cfg & AREPI_TILE_PAIRED_ROWS)
         return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_ring: AREPI_TILE_PAIRED_ROWS applies to the direct form only");
+    if (tile_cfg & AREPI_TILE_OWNER_FIRST)
+        return fail(AREPI_EINVAL, "arepi_gemm_rs_ring: AREPI_TILE_OWNER_FIRST is not an option of the ring order");
     int rc = arepi_gemm_rs_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish, tile_cfg);
     if (rc) return rc;
     if (R > 1 && (M / R) % kRingRowAlign)

@@ -18,6 +18,7 @@ launch time, against the MFMA or HBM peak) and, where the oracle has one, a
 bounded `cpu_baseline`:
   gemm_rs_tiny          R=2, X[256,256], W[256,512] (launch-bound)
   gemm_rs_tp4_prestaged the headline's kernel with every partial landed
+  gemm_plain_tp4        the same kernel with R=1 (the plain product), beside the library's
   gemm_rs_tp8_m{M}      R=8, X[M,2048], W[2048,7168], M = 256, 1024, 4096, 8192
   lamport_ar_rmsnorm    8 x [4096,7168] partials, RMSNorm over 7168
   combine_reduce        [4096,8,7168] top-8 weighted sum, register pipeline and
@@ -62,8 +63,8 @@ PRODUCER_TILES_PER_RELEASE = 8
 # of them have started, so a small persistent grid also keeps the gate short.
 PRODUCER_WORKGROUPS = 96
 
-LEGS = ("gemm_rs", "gemm_rs_tiny", "gemm_rs_prestaged", "gemm_rs_tp8", "lamport", "combine", "combine_lds",
-        "lamport_2phase", "gemm_rs_fp8", "gemm_rs_ring", "gemm_rs_ring_prestaged")
+LEGS = ("gemm_rs", "gemm_rs_tiny", "gemm_rs_prestaged", "gemm_plain", "gemm_rs_tp8", "lamport", "combine",
+        "combine_lds", "lamport_2phase", "gemm_rs_fp8", "gemm_rs_ring", "gemm_rs_ring_prestaged")
 
 _side_stream = None
 
@@ -357,6 +358,24 @@ def gemm_rs_prestaged(A, inputs, torch, iters, warmup, num, M=None, ring=False, 
     return res
 
 
+def gemm_plain(A, torch, iters, warmup, M=4096, N=4096, K=2048):
+    """Context: the same kernel with R = 1 (no peers, no send: the plain
+    product X.W into out) beside the library's plain product of the same
+    shape, so the two mainloops compare directly."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(1010)
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16).to(dev)
+    w = (torch.randn(K, N, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    tile = A.gemm_rs_pick_tile(M, N, K, 1, 0)
+    st = time_launches(torch, lambda: A.gemm_rs_fused(x, w, [None], None, out, 1, 0, tile=tile), iters, warmup)
+    flops = 2.0 * M * N * K
+    t = st["ms_median"] * 1e-3
+    return dict(M=M, N=N, K=K, R=1, tile=A.TILE_NAMES[tile], **st, tflops=flops / t / 1e12,
+                roofline=roofline("mfma", flops, st, PEAK_BF16_TFLOPS, "TFLOP/s", None, "gemm_rs_kernel"),
+                library_gemm=library_gemm(torch, x, w, iters, warmup))
+
+
 def library_gemm(torch, x, w, iters, warmup):
     """Context only: the plain product X.W of the same shape through
     torch.matmul (hipBLASLt), no reduce-scatter -- what a library GEMM alone
@@ -595,6 +614,8 @@ def main():
         secondary["gemm_rs_tiny"] = gemm_rs_prestaged(A, inputs, torch, it, wu, 1)
     if run("gemm_rs_prestaged") or run("gemm_rs"):
         secondary["gemm_rs_tp4_prestaged"] = gemm_rs_prestaged(A, inputs, torch, it, wu, 2, counters="gemm_rs_tp4")
+    if run("gemm_plain"):
+        secondary["gemm_plain_tp4"] = gemm_plain(A, torch, it, wu)
     if run("gemm_rs_tp8"):
         for m in ([a.m] if a.m else inputs.TP8_M_SWEEP):
             key = "gemm_rs_tp8_m%d" % m

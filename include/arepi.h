@@ -86,7 +86,16 @@ enum {
      * ready_in bit they waited for, so ready_in is all zero again when the
      * call ends and the next call can use it without a separate clear.  Needs
      * the flag tiles to nest inside the compute tiles, as ready_out does. */
-    AREPI_TILE_CONSUME_READY = 0x400
+    AREPI_TILE_CONSUME_READY = 0x400,
+    /* ORed into a contiguous tile_cfg (AUTO included) of arepi_gemm_rs_fused:
+     * the owner segment's row blocks come first in the schedule instead of
+     * last.  Last suits partials that land while the GEMM runs (the owner
+     * tiles wait for them as late as possible); first suits partials already
+     * landed when the call starts: in a grid of several rounds the owner
+     * tiles' longer epilogue (R-1 partials read per tile) then overlaps the
+     * later rounds instead of forming the last one.  Not with
+     * AREPI_TILE_PAIRED_ROWS, not for the push ring or the fp8 form. */
+    AREPI_TILE_OWNER_FIRST = 0x800
 };
 
 /* Message describing the last failed call on this thread ("" if none). */

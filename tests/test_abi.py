@@ -265,6 +265,40 @@ def test_consume_option_plans_like_publication(M, N, R):
         assert np.array_equal(ref, got)
 
 
+@pytest.mark.parametrize("M,N,R,owner", [(4096, 7168, 8, 3), (8192, 7168, 8, 0), (1024, 7168, 8, 5),
+                                         (4096, 4096, 4, 0), (520, 1032, 8, 4), (200, 520, 2, 1)])
+def test_owner_first_reorders_the_same_tiles(M, N, R, owner):
+    """AREPI_TILE_OWNER_FIRST keeps the tile set and layout and moves the
+    workgroups holding owner rows ahead of the rest; where the default order
+    leaves them for a second round of 256 workgroups, the owner-first order
+    puts them all in the first."""
+    seg = M // R
+    pub = A.gemm_rs_supports(M, N, 2048, R, owner, publish=True) == 0
+    base = np.asarray(A.gemm_rs_schedule(M, N, 2048, R, owner, publish=pub))
+    first = np.asarray(A.gemm_rs_schedule(M, N, 2048, R, owner, publish=pub, tile=A.TILE_OWNER_FIRST))
+    assert sorted(map(tuple, base.tolist())) == sorted(map(tuple, first.tolist()))
+
+    def owner_rows(s):
+        return np.array([a0 // seg == owner or (blen > 0 and b0 // seg == owner) for _, _, a0, _, b0, blen in s])
+    ob, of = owner_rows(base), owner_rows(first)
+    idx = np.arange(len(base))
+    if ob.all():
+        return  # one segment holds every tile: nothing to reorder
+    assert idx[of].mean() < idx[~of].mean() and idx[ob].mean() > idx[~ob].mean()
+    if len(base) > 256 and of.sum() <= 256:
+        assert idx[of].max() < 256 and idx[ob].min() >= len(base) - 256 - 32
+
+
+def test_owner_first_refuses_paired_rows_ring_and_fp8():
+    t = A.TILE_OWNER_FIRST
+    assert A.gemm_rs_supports(4096, 4096, 2048, 4, 0, publish=True, tile=t) == 0
+    assert A.gemm_rs_supports(4096, 4096, 2048, 4, 0, publish=True, tile=t | A.TILE_PAIRED_ROWS) == A.EINVAL
+    assert "contiguous" in A.last_error()
+    assert A.gemm_rs_ring_supports(4096, 4096, 2048, 4, 0, publish=True, tile=t) == A.EINVAL
+    assert "ring" in A.last_error()
+    assert A.gemm_rs_fp8_supports(512, 512, 256, 2, 0, tile=t) != 0
+
+
 @pytest.mark.parametrize("M,N,R,owner", [(256, 512, 2, 0), (4096, 4096, 4, 0), (256, 7168, 8, 0), (96, 72, 4, 2)])
 def test_ring_supports_follows_the_direct_form(M, N, R, owner):
     """The push-ring form accepts what the direct form accepts (contiguous

@@ -126,6 +126,23 @@ def test_paired_half_blocks_every_tile(M, N, K, R, owner, ftm, ftn):
         check_against_oracle(case, res, ftm, ftn, what="paired/%s" % tile_name(tile), ref=ref)
 
 
+@pytest.mark.parametrize("M,N,K,R,owner,ftm,ftn", [
+    (200, 520, 200, 2, 1, 32, 64),       # ragged M tile, N and K tails
+    (520, 1032, 72, 8, 4, 128, 128),     # segments straddling every tile
+    (4096, 7168, 256, 8, 3, 128, 128),   # several rounds of workgroups at the model width
+])
+def test_owner_first_order_every_tile(M, N, K, R, owner, ftm, ftn):
+    """AREPI_TILE_OWNER_FIRST changes only the order of the workgroups."""
+    case = inputs.gemm_rs_case(M, N, K, R, owner=owner, seed=13 + M + N + K)
+    ref = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
+    for base in [A.TILE_AUTO] + sorted(A.TILE_NAMES):
+        tile = base | A.TILE_OWNER_FIRST
+        pub = A.gemm_rs_supports(M, N, K, R, owner, ftm, ftn, publish=True, tile=tile) == 0
+        print("owner-first %s tile=%s publish=%s" % ((M, N, K, R, owner), tile_name(base), pub), flush=True)
+        res = run(case, tile=tile, publish=pub, ftm=ftm, ftn=ftn)
+        check_against_oracle(case, res, ftm, ftn, what="owner-first/%s" % tile_name(base), ref=ref)
+
+
 def test_golden_all_ones_two_ranks_on_gpu():
     g = read_golden("gemm_ar_all_ones.txt")
     M, N, K, R = g["M"], g["N"], g["K"], g["ranks"]
@@ -326,16 +343,18 @@ def test_gate_times_out_when_no_producer_announces():
     assert int(status.item()) & A.STATUS_TIMEOUT
 
 
-@pytest.mark.parametrize("M,owner", [(256, 0), (1024, 0), (1024, 7), (4096, 0), (8192, 0)])
-def test_tp8_workload_sweep(M, owner):
+@pytest.mark.parametrize("M,owner,tile", [(256, 0, A.TILE_AUTO), (1024, 0, A.TILE_AUTO), (1024, 7, A.TILE_AUTO),
+                                          (4096, 0, A.TILE_AUTO), (8192, 0, A.TILE_AUTO),
+                                          (4096, 5, A.TILE_OWNER_FIRST), (8192, 0, A.TILE_OWNER_FIRST)])
+def test_tp8_workload_sweep(M, owner, tile):
     case = inputs.workload_gemm_rs(3, M=M, owner=owner)
     R = 8
     seg = M // R
-    res = run(case)
+    res = run(case, tile=tile)
     rows = [(owner * seg, (owner + 1) * seg)]
     rows += [(d * seg, d * seg + min(8, seg)) for d in range(R) if d != owner]
     rows += [(d * seg + seg - min(8, seg), d * seg + seg) for d in range(R) if d != owner]
-    check_against_oracle(case, res, rows=rows, what="tp8 M=%d" % M)
+    check_against_oracle(case, res, rows=rows, what="tp8 M=%d tile=%#x" % (M, tile))
 
 
 def test_timeout_reports_status_and_finishes():
