@@ -26,7 +26,8 @@ OK, EINVAL, EUNSUPPORTED, ELAUNCH = 0, -1, -2, -3
 SCOPE_AGENT, SCOPE_SYSTEM = 0, 1
 STATUS_TIMEOUT = 1
 (TILE_AUTO, TILE_256x256, TILE_128x256, TILE_128x128, TILE_64x128, TILE_32x256, TILE_256x256_S4,
- TILE_256x128_S3, TILE_128x256_S3, TILE_128x128_S4, TILE_256x256_W8, TILE_256x256_W8_K64) = range(12)
+ TILE_256x128_S3, TILE_128x256_S3, TILE_128x128_S4, TILE_256x256_W8, TILE_256x256_W8_K64,
+ TILE_64x128_S4) = range(13)
 TILE_PAIRED_ROWS = 0x200  # OR into an explicit tile: pair owner half-blocks with non-owner ones
 TILE_CONSUME_READY = 0x400  # OR into any tile: owner tiles clear the ready_in bits they waited for
 TILE_OWNER_FIRST = 0x800  # OR into a contiguous tile: the owner's row blocks first (partials already landed)
@@ -34,11 +35,11 @@ LAMPORT_NOALLOC_BYTES = 32 * 1024 * 1024  # static staging of ar_rmsnorm_lamport
 TILE_NAMES = {TILE_256x256: "256x256", TILE_128x256: "128x256", TILE_128x128: "128x128",
               TILE_64x128: "64x128", TILE_32x256: "32x256", TILE_256x256_S4: "256x256_s4",
               TILE_256x128_S3: "256x128_s3", TILE_128x256_S3: "128x256_s3", TILE_128x128_S4: "128x128_s4", TILE_256x256_W8: "256x256_w8",
-              TILE_256x256_W8_K64: "256x256_w8_k64"}
+              TILE_256x256_W8_K64: "256x256_w8_k64", TILE_64x128_S4: "64x128_s4"}
 TILE_DIMS = {TILE_256x256: (256, 256), TILE_128x256: (128, 256), TILE_128x128: (128, 128),
              TILE_64x128: (64, 128), TILE_32x256: (32, 256), TILE_256x256_S4: (256, 256),
              TILE_256x128_S3: (256, 128), TILE_128x256_S3: (128, 256), TILE_128x128_S4: (128, 128), TILE_256x256_W8: (256, 256),
-             TILE_256x256_W8_K64: (256, 256)}
+             TILE_256x256_W8_K64: (256, 256), TILE_64x128_S4: (64, 128)}
 
 _lock = threading.Lock()
 _lib = None

@@ -1131,9 +1131,13 @@ struct TileCfg {
     int id, BM, BN;
     int slots;   // workgroups co-resident on one CU (LDS / register bound)
     double eff;  // relative per-CU throughput used by the automatic choice
+    bool one_wave = false;  // chosen automatically only when every tile is resident at once
 };
 // eff: sustained per-CU throughput relative to the 4-stage 256x256 tile, from
-// timing the tp=4 / tp=8 workloads on MI355X (contiguous rows).
+// timing the tp=4 / tp=8 workloads on MI355X (contiguous rows).  64x128_s4
+// beats 64x128 when each CU runs one tile (tp=8 M=256: 32 against 34.5 us)
+// and loses when a CU has two (M=512: 54 against 44 us, where 64x128 keeps
+// both resident side by side), hence one_wave.
 constexpr TileCfg kTiles[] = {
     {AREPI_TILE_256x256_W8_K64, 256, 256, 1, 1.14},
     {AREPI_TILE_256x256_W8, 256, 256, 1, 1.08},
@@ -1144,6 +1148,7 @@ constexpr TileCfg kTiles[] = {
     {AREPI_TILE_128x256_S3, 128, 256, 2, 0.93},
     {AREPI_TILE_128x128_S4, 128, 128, 2, 0.80},
     {AREPI_TILE_128x128, 128, 128, 2, 0.75},
+    {AREPI_TILE_64x128_S4, 64, 128, 1, 0.64, true},
     {AREPI_TILE_64x128, 64, 128, 3, 0.60},
     {AREPI_TILE_32x256, 32, 256, 2, 0.40},
 };
@@ -1214,6 +1219,7 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, bool pub
         if (publish && !flags_nest(M, N, R, ftm, ftn, t.BM, t.BN)) continue;
         if (whole_segments && R > 1 && (M / R) % t.BM) continue;
         const int64_t count = cdiv(M, t.BM) * cdiv(N, t.BN);
+        if (t.one_wave && count > 256 * (int64_t)t.slots) continue;
         // waves of co-resident tiles x time of one wave; a wave with fewer
         // tiles than slots on each CU runs fewer of them side by side
         const int64_t waves = cdiv(count, 256 * (int64_t)t.slots);

@@ -83,6 +83,7 @@ bool launch_tile(int cfg, const GemmRsParams &p, hipStream_t s) {
         case AREPI_TILE_128x128_S4: launch<128, 128, 64, 64, 32, 4, 2, MIXED>(p, s); return true;
         case AREPI_TILE_256x256_W8: launch<256, 256, 128, 64, 32, 4, 2, MIXED>(p, s); return true;
         case AREPI_TILE_256x256_W8_K64: launch<256, 256, 128, 64, 64, 2, 2, MIXED>(p, s); return true;
+        case AREPI_TILE_64x128_S4: launch<64, 128, 32, 64, 64, 4, 0, MIXED>(p, s); return true;
         default: return false;
     }
 }

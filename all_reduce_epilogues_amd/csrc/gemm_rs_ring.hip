@@ -164,6 +164,7 @@ extern "C" int arepi_gemm_rs_ring(const uint16_t *x, const uint16_t *w, const ui
         case AREPI_TILE_128x128_S4: launch_ring<128, 128, 64, 64, 32, 4, 2>(p, s); break;
         case AREPI_TILE_256x256_W8: launch_ring<256, 256, 128, 64, 32, 4, 2>(p, s); break;
         case AREPI_TILE_256x256_W8_K64: launch_ring<256, 256, 128, 64, 64, 2, 2>(p, s); break;
+        case AREPI_TILE_64x128_S4: launch_ring<64, 128, 32, 64, 64, 4, 0>(p, s); break;
         default: return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_ring: no kernel for tile " + std::to_string(c.id));
     }
     return check_launch("arepi_gemm_rs_ring");

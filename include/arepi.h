@@ -61,7 +61,8 @@ enum { AREPI_STATUS_TIMEOUT = 1u };
 
 /* Compute-tile choice for arepi_gemm_rs_fused (0 = chosen from the shape).
  * BMxBN is the output tile of one workgroup; the _S variants walk K in
- * 32-wide steps through an S-stage LDS ring (the others: 64-wide, 2 stages). */
+ * 32-wide steps through an S-stage LDS ring (the others: 64-wide, 2 stages;
+ * 64x128_S4: 64-wide, 4 stages). */
 enum {
     AREPI_TILE_AUTO = 0,
     AREPI_TILE_256x256 = 1,
@@ -75,6 +76,7 @@ enum {
     AREPI_TILE_128x128_S4 = 9,
     AREPI_TILE_256x256_W8 = 10, /* 8 waves (two per SIMD), BK 32, 4 stages */
     AREPI_TILE_256x256_W8_K64 = 11, /* 8 waves, BK 64, 2 stages: half the barriers per K */
+    AREPI_TILE_64x128_S4 = 12,      /* BK 64, 4 stages (96 KiB of LDS): one workgroup per CU */
     /* ORed into an explicit tile: when every segment is a whole number of
      * half-blocks (BM/2 rows, BM >= 64), a workgroup takes two half-blocks and
      * the owner segment's half-blocks are each paired with a non-owner one,
