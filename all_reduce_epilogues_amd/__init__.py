@@ -93,7 +93,7 @@ def lib():
                                          vp], i32),
             "arepi_emu_producer_gate": ([vp, u32p, i64, vp], i32),
             "arepi_emu_peer_producer_steps": ([vp, vp, vp, vp, i32, i64, i64, i64, i32, i32, i32, i32, i32, i32,
-                                               i32, vp, vp, i32, u32p, i64, vp], i32),
+                                               i32, vp, vp, i32, i32, i64, u32p, i64, vp], i32),
             "arepi_emu_signal": ([vp, ctypes.c_uint32, vp], i32),
             "arepi_emu_stream_create": ([vp], i32),
             "arepi_emu_stream_destroy": ([vp], i32),
@@ -363,13 +363,13 @@ def emu_peer_producer(src, recv, ready_in, order, R: int, owner: int, M: int, N:
     _check(rc, "emu_peer_producer")
 
 
-def _peer_arrays(src, recv, R, owner, seg, N):
+def _peer_arrays(src, recv, R, owner, seg, N, src_sets=0):
     sp = (ctypes.c_void_p * R)()
     rp = (ctypes.c_void_p * R)()
     for p in range(R):
         if p == owner:
             continue
-        _bf16(src[p], "src[%d]" % p, (seg, N))
+        _bf16(src[p], "src[%d]" % p, (src_sets, seg, N) if src_sets else (seg, N))
         _bf16(recv[p], "recv[%d]" % p, (seg, N))
         sp[p] = src[p].data_ptr()
         rp[p] = recv[p].data_ptr()
@@ -379,10 +379,15 @@ def _peer_arrays(src, recv, R, owner, seg, N):
 def emu_peer_producer_steps(src, recv, ready_in, orders, R: int, owner: int, M: int, N: int, go, steps: int,
                             flag_tile_m: int = 128, flag_tile_n: int = 128, scope: int = SCOPE_AGENT,
                             workgroups: int = 0, items_per_release: int = 1, resident=None, status=None,
-                            spin_limit: int = 0, stream=None):
+                            spin_limit: int = 0, stream=None, credit: bool = False):
     """Test-only: the emulated peers of `steps` consecutive calls in one launch;
-    step s lands orders[s % len(orders)] once go[0] >= s (raise it with
-    emu_signal after each call).  orders: int32 [n_orders, n_items, 2]."""
+    step s lands orders[s % len(orders)] (orders: int32 [n_orders, n_items,
+    2]).  go: uint32 [1], zero before the launch.  credit=False: step s starts
+    once go[0] >= s (raise it with emu_signal after each call).  credit=True:
+    go counts the producer's own landed steps, and each batch waits until its
+    ready_in bits have been consumed (the consumer passes TILE_CONSUME_READY).
+    src[p]: bf16 [M/R, N], the same every step, or [n_orders, M/R, N], set
+    s % n_orders for step s."""
     torch = _torch()
     _need(orders, "orders", (torch.int32,))
     if orders.dim() != 3 or orders.shape[2] != 2:
@@ -390,15 +395,18 @@ def emu_peer_producer_steps(src, recv, ready_in, orders, R: int, owner: int, M: 
     words = gemm_rs_flag_words(M, N, R, flag_tile_m, flag_tile_n)
     _flags(ready_in, "ready_in", (R, words))
     _flags(go, "go", (1,))
+    some = next(src[p] for p in range(R) if p != owner)
+    sets = orders.shape[0] if some.dim() == 3 else 0
     if resident is not None:
         _flags(resident, "resident", (2,))
     if status is not None:
         _flags(status, "status", (1,))
-    sp, rp = _peer_arrays(src, recv, R, owner, M // R, N)
+    sp, rp = _peer_arrays(src, recv, R, owner, M // R, N, sets)
     rc = lib().arepi_emu_peer_producer_steps(sp, rp, _ptr(ready_in), _ptr(orders), orders.shape[0], orders.shape[1],
                                              M, N, R, owner, flag_tile_m, flag_tile_n, scope, workgroups,
-                                             items_per_release, _ptr(resident), _ptr(go), steps, _ptr(status),
-                                             spin_limit, _stream(stream))
+                                             items_per_release, _ptr(resident), _ptr(go), int(bool(credit)), steps,
+                                             (M // R) * N if sets else 0, _ptr(status), spin_limit,
+                                             _stream(stream))
     _check(rc, "emu_peer_producer_steps")
 
 

@@ -27,10 +27,19 @@ struct EmuParams {
     int ftm, ftn, R, owner, system_scope;
     int per_release;  // items landed per release
     uint32_t *resident;  // NULL, or [2]: workgroups started, grid size
-    // several steps in one launch: step s uses order s % n_orders and starts
-    // once *go >= s (go NULL: one step, no wait)
-    const uint32_t *go;
+    // several steps in one launch: step s uses order s % n_orders.  Signal
+    // mode: step s starts once *go >= s (go NULL: no wait).  Credit mode: go
+    // counts the producer's own (workgroup, step) completions; step s starts
+    // once every workgroup has finished step s-1 (*go >= s * grid), then each
+    // batch waits until its items' bits are clear (the consumer clears a bit
+    // once it has read that tile).  Both are needed: with the order changing
+    // between steps, a bit that is clear because another workgroup has not
+    // yet landed that tile for step s-1 is not a credit.
+    uint32_t *go;
     int steps, n_orders;
+    int credit;
+    // step s copies from src[peer] + (s % n_orders) * src_step elements
+    int64_t src_step;
     uint32_t *status;
     int64_t spin_limit;
 };
@@ -42,7 +51,7 @@ __device__ bool item_valid(const EmuParams &p, const int32_t *order, const int64
 }
 
 // Copies one (peer, flag tile) item with the whole workgroup (no drain).
-__device__ void copy_item(const EmuParams &p, const int32_t *order, const int64_t item) {
+__device__ void copy_item(const EmuParams &p, const int32_t *order, const int64_t item, const int64_t src_off) {
     int peer;
     int64_t t;
     if (!item_valid(p, order, item, peer, t)) return;  // uniform across the workgroup
@@ -54,7 +63,7 @@ __device__ void copy_item(const EmuParams &p, const int32_t *order, const int64_
 #pragma unroll
     for (int i = 0; i < kMaxR; ++i)
         if (i == peer) {
-            s = p.src[i];
+            s = p.src[i] + src_off;
             d = p.recv[i];
         }
     // 16-byte packs, eight per thread in flight (streaming loads and stores).
@@ -103,12 +112,15 @@ __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
     const bool sys = p.system_scope != 0;
     for (int st = 0; st < p.steps; ++st) {
         if (p.go) {
-            // wait for the consumer of step st-1 to be done with recv and ready_in
+            // signal mode: wait for the consumer of step st-1 to be done with
+            // recv and ready_in; credit mode: wait for every producer
+            // workgroup to have landed step st-1
+            const uint32_t need = p.credit ? (uint32_t)st * gridDim.x : (uint32_t)st;
             if (threadIdx.x == 0) {
                 int64_t n = 0;
                 const uint64_t t0 = spin_clock();
                 stop = 0;
-                while (load_relaxed(p.go, false) < (uint32_t)st) {
+                while (load_relaxed(p.go, false) < need) {
                     if (spin_expired(p.spin_limit, n, t0)) {
                         stop = 1;
                         if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
@@ -121,9 +133,40 @@ __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
             if (stop) return;
         }
         const int32_t *order = p.order + (int64_t)(st % p.n_orders) * p.n_items * 2;
+        const int64_t src_off = (int64_t)(st % p.n_orders) * p.src_step;
         for (int64_t j = blockIdx.x; j < batches; j += gridDim.x) {
             const int64_t i0 = j * K, i1 = min(i0 + K, p.n_items);
-            for (int64_t item = i0; item < i1; ++item) copy_item(p, order, item);
+            if (p.credit) {
+                // wait until the consumer has read what the batch's slots hold
+                // (a bit still set belongs to the previous step); the copies
+                // below are issued only once the loop has seen every bit clear
+                if (threadIdx.x < 64) {
+                    int64_t n = 0;
+                    const uint64_t t0 = spin_clock();
+                    bool expired = false;
+                    for (int64_t item = i0 + threadIdx.x; item < i1 && !expired; item += 64) {
+                        int peer;
+                        int64_t t;
+                        if (!item_valid(p, order, item, peer, t)) continue;
+                        const uint32_t *w = p.ready_in + (int64_t)peer * p.fwords + (t >> 5);
+                        while (load_relaxed(w, sys) & (1u << (t & 31))) {
+                            if (spin_expired(p.spin_limit, n, t0)) {
+                                expired = true;
+                                break;
+                            }
+                            __builtin_amdgcn_s_sleep(2);
+                        }
+                    }
+                    const bool any = __builtin_amdgcn_ballot_w64(expired) != 0;
+                    if (threadIdx.x == 0) {
+                        stop = any ? 1 : 0;
+                        if (any && p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
+                    }
+                }
+                __syncthreads();
+                if (stop) return;
+            }
+            for (int64_t item = i0; item < i1; ++item) copy_item(p, order, item, src_off);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (threadIdx.x == 0) {
@@ -135,6 +178,12 @@ __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
                         fetch_or_relaxed(p.ready_in + (int64_t)peer * p.fwords + (t >> 5), 1u << (t & 31), sys);
                 }
             }
+        }
+        if (p.credit && threadIdx.x == 0) {
+            // this workgroup's bits of step st are set (the atomics have
+            // completed) before it counts the step as landed
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __hip_atomic_fetch_add(p.go, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -178,8 +227,8 @@ using namespace arepi;
 static int emu_launch(const char *who, const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
                       const int32_t *order, int64_t n_items, int64_t M, int64_t N, int R, int owner,
                       int flag_tile_m, int flag_tile_n, int scope, int workgroups, int items_per_release,
-                      uint32_t *resident, const uint32_t *go, int steps, int n_orders, uint32_t *status,
-                      int64_t spin_limit, arepi_stream_t stream) {
+                      uint32_t *resident, uint32_t *go, int steps, int n_orders, bool credit,
+                      int64_t src_step, uint32_t *status, int64_t spin_limit, arepi_stream_t stream) {
     auto bad = [who](const std::string &m) { return fail(AREPI_EINVAL, std::string(who) + ": " + m); };
     if (R < 1 || R > kMaxR) return bad("R=" + std::to_string(R) + " outside [1, 8]");
     if (owner < 0 || owner >= R) return bad("owner outside [0, R-1]");
@@ -192,6 +241,7 @@ static int emu_launch(const char *who, const uint16_t *const *src, uint16_t *con
     if (workgroups < 0) return bad("workgroups must be >= 0 (0: one per batch)");
     if (items_per_release < 1) return bad("items_per_release must be >= 1");
     if (steps < 1 || n_orders < 1) return bad("steps and n_orders must be >= 1");
+    if (src_step < 0 || src_step % 8) return bad("src_step must be a non-negative multiple of 8");
     if (n_items == 0) return ok();
     if (!src || !recv || !ready_in || !order) return bad("src, recv, ready_in and order must be non-NULL");
     EmuParams p{};
@@ -220,6 +270,8 @@ static int emu_launch(const char *who, const uint16_t *const *src, uint16_t *con
     p.go = go;
     p.steps = steps;
     p.n_orders = n_orders;
+    p.credit = credit ? 1 : 0;
+    p.src_step = src_step;
     p.status = status;
     p.spin_limit = spin_bound(spin_limit);
     const int64_t batches = (n_items + items_per_release - 1) / items_per_release;
@@ -236,20 +288,21 @@ extern "C" int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *con
                                        arepi_stream_t stream) {
     return emu_launch("arepi_emu_peer_producer", src, recv, ready_in, order, n_items, M, N, R, owner,
                       flag_tile_m, flag_tile_n, scope, workgroups, items_per_release, resident, nullptr, 1, 1,
-                      nullptr, 0, stream);
+                      false, 0, nullptr, 0, stream);
 }
 
 extern "C" int arepi_emu_peer_producer_steps(const uint16_t *const *src, uint16_t *const *recv,
                                              uint32_t *ready_in, const int32_t *orders, int n_orders,
                                              int64_t n_items, int64_t M, int64_t N, int R, int owner,
                                              int flag_tile_m, int flag_tile_n, int scope, int workgroups,
-                                             int items_per_release, uint32_t *resident, const uint32_t *go,
-                                             int steps, uint32_t *status, int64_t spin_limit,
+                                             int items_per_release, uint32_t *resident, uint32_t *go, int credit,
+                                             int steps, int64_t src_step, uint32_t *status, int64_t spin_limit,
                                              arepi_stream_t stream) {
     if (!go) return fail(AREPI_EINVAL, "arepi_emu_peer_producer_steps: go must be non-NULL");
+    if (credit != 0 && credit != 1) return fail(AREPI_EINVAL, "arepi_emu_peer_producer_steps: credit must be 0 or 1");
     return emu_launch("arepi_emu_peer_producer_steps", src, recv, ready_in, orders, n_items, M, N, R, owner,
                       flag_tile_m, flag_tile_n, scope, workgroups, items_per_release, resident, go, steps,
-                      n_orders, status, spin_limit, stream);
+                      n_orders, credit != 0, src_step, status, spin_limit, stream);
 }
 
 extern "C" int arepi_emu_signal(uint32_t *flag, uint32_t value, arepi_stream_t stream) {

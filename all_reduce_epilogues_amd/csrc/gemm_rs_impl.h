@@ -739,13 +739,16 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     // the tile's rows as up to two ranges [r0[h], r1[h]) (one when B follows
     // A; empty ranges have r0 == r1); loops over h are unrolled so that these
     // stay in registers
+    auto row_ranges = [](int xa0, int xalen, int xb0, int xblen, int (&q0)[2], int (&q1)[2]) {
+        if (xalen > 0 && xblen > 0 && xb0 == xa0 + xalen) {
+            q0[0] = xa0, q1[0] = xa0 + xalen + xblen, q0[1] = q1[1] = 0;
+        } else {
+            q0[0] = xa0, q1[0] = xa0 + max(xalen, 0);
+            q0[1] = xb0, q1[1] = xb0 + max(xblen, 0);
+        }
+    };
     int r0[2], r1[2];
-    if (alen > 0 && blen > 0 && (int)b0 == (int)a0 + alen) {
-        r0[0] = (int)a0, r1[0] = (int)a0 + alen + blen, r0[1] = r1[1] = 0;
-    } else {
-        r0[0] = (int)a0, r1[0] = (int)a0 + max(alen, 0);
-        r0[1] = (int)b0, r1[1] = (int)b0 + max(blen, 0);
-    }
+    row_ranges((int)a0, alen, (int)b0, blen, r0, r1);
     constexpr bool has_owner = KIND != kNoOwnerRows;  // tiles that wait for and add partials
     constexpr bool kRingK = KIND == kRing;
     bool has_other = false;
@@ -753,66 +756,47 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
     for (int h = 0; h < 2; ++h) has_other |= r0[h] < r1[h] && (r0[h] < oseg0 || r1[h] > oseg1);
     const int tc0 = (int)(n0 / p.ftn), ntc = (int)((min(n0 + BN, N) - 1) / p.ftn) - tc0 + 1;
 
-    auto wait_ready = [&]() {
-    if constexpr (has_owner) {
-        // Wait until every flag tile this tile adds is set: one (source, flag
-        // tile) item per lane, all polled at once with relaxed loads, then one
-        // acquire.  Each flag tile lies under exactly one workgroup's rows and
-        // columns when bits are consumed (checked on the host), so no other
-        // workgroup waits for the bits cleared here; the kernel's end makes the
-        // clears visible to whatever the stream runs next.
-        if (wave == 0) {
-            auto wait_items = [&](int items, auto item) {
-                int64_t spins = 0;
-                const uint64_t t0 = spin_clock();
-                for (int k = lane; k < items; k += 64) {
-                    uint32_t *word, bit;
-                    item(k, word, bit);
-                    while (!(load_relaxed(word, sys) & bit)) {
-                        if (spin_expired(p.spin_limit, spins, t0)) {
-                            if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
-                            break;
+    // The (source, flag tile) items this tile adds: with_items(fn) calls
+    // fn(count, item), item(k, word, bit) giving item k's ready_in word and bit.
+    // (The row ranges are recomputed here, so that they need not stay live
+    // through the drain for the clears at the end.)
+    auto with_items = [&](bool launder, auto &&fn) {
+        // launder: hide the tile's row ranges from the compiler, so that
+        // nothing computed from them for the wait is kept live to the end
+        int xa0 = (int)a0, xalen = alen, xb0 = (int)b0, xblen = blen;
+        if (launder) asm volatile("" : "+s"(xa0), "+s"(xalen), "+s"(xb0), "+s"(xblen));
+        int r0[2], r1[2];
+        row_ranges(xa0, xalen, xb0, xblen, r0, r1);
+        if constexpr (kRingK) {
+            // Ring: the flag tiles of the upstream partial of every segment
+            // the tile's rows touch, except the chain segment.  Walks the
+            // (range, segment) pieces in order; returns the item count and,
+            // for 0 <= k < count, item k's word and bit.
+            auto walk = [&](int k, uint32_t *&word, uint32_t &bit) {
+                int seen = 0;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (r0[h] >= r1[h]) continue;
+                    const int d0 = r0[h] / seg, d1 = (r1[h] - 1) / seg;
+                    for (int d = d0; d <= d1; ++d) {
+                        if (d == p.chain) continue;
+                        const int s0 = d * seg;
+                        const int lr0 = max(r0[h], s0) - s0, lr1 = min(r1[h], s0 + seg) - s0;
+                        const int tr0 = lr0 / p.ftm, n = ((lr1 - 1) / p.ftm - tr0 + 1) * ntc;
+                        if (k >= seen && k < seen + n) {
+                            const int ti = k - seen;
+                            const int t = (tr0 + ti / ntc) * (int)p.ftiles_n + tc0 + ti % ntc;
+                            word = p.ready_in + (int64_t)d * p.fwords + (t >> 5);
+                            bit = 1u << (t & 31);
                         }
-                        __builtin_amdgcn_s_sleep(2);
+                        seen += n;
                     }
                 }
-                if (p.consume)
-                    for (int k = lane; k < items; k += 64) {
-                        uint32_t *word, bit;
-                        item(k, word, bit);
-                        fetch_and_relaxed(word, ~bit, sys);
-                    }
+                return seen;
             };
-            if constexpr (kRingK) {
-                // Ring: the flag tiles of the upstream partial of every segment
-                // the tile's rows touch, except the chain segment.  Walks the
-                // (range, segment) pieces in order; returns the item count and,
-                // for 0 <= k < count, item k's word and bit.
-                auto walk = [&](int k, uint32_t *&word, uint32_t &bit) {
-                    int seen = 0;
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        if (r0[h] >= r1[h]) continue;
-                        const int d0 = r0[h] / seg, d1 = (r1[h] - 1) / seg;
-                        for (int d = d0; d <= d1; ++d) {
-                            if (d == p.chain) continue;
-                            const int s0 = d * seg;
-                            const int lr0 = max(r0[h], s0) - s0, lr1 = min(r1[h], s0 + seg) - s0;
-                            const int tr0 = lr0 / p.ftm, n = ((lr1 - 1) / p.ftm - tr0 + 1) * ntc;
-                            if (k >= seen && k < seen + n) {
-                                const int ti = k - seen;
-                                const int t = (tr0 + ti / ntc) * (int)p.ftiles_n + tc0 + ti % ntc;
-                                word = p.ready_in + (int64_t)d * p.fwords + (t >> 5);
-                                bit = 1u << (t & 31);
-                            }
-                            seen += n;
-                        }
-                    }
-                    return seen;
-                };
-                uint32_t *w0 = nullptr, b0_ = 0;
-                wait_items(walk(-1, w0, b0_), walk);
-            } else {
+            uint32_t *w0 = nullptr, b0_ = 0;
+            fn(walk(-1, w0, b0_), walk);
+        } else {
             int tr0[2] = {0, 0}, th[2] = {0, 0};
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -833,11 +817,55 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
                 word = p.ready_in + (int64_t)rank * p.fwords + (t >> 5);
                 bit = 1u << (t & 31);
             };
-            wait_items(items, item);
-            }
+            fn(items, item);
+        }
+    };
+
+    auto wait_ready = [&]() {
+    if constexpr (has_owner) {
+        // Wait until every flag tile this tile adds is set: one item per
+        // lane, all polled at once with relaxed loads, then one acquire.
+        if (wave == 0) {
+            with_items(false, [&](int items, auto item) {
+                int64_t spins = 0;
+                const uint64_t t0 = spin_clock();
+                for (int k = lane; k < items; k += 64) {
+                    uint32_t *word, bit;
+                    item(k, word, bit);
+                    while (!(load_relaxed(word, sys) & bit)) {
+                        if (spin_expired(p.spin_limit, spins, t0)) {
+                            if (p.status) atomicOr(p.status, (uint32_t)AREPI_STATUS_TIMEOUT);
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+            });
             fence_acquire(sys);
         }
         __syncthreads();
+    }
+    };
+
+    // Consumption: clear the bits waited for, at the end of the tile, once
+    // every wave has drained (barrier): by then every load of the peers' data
+    // has returned, so a bit that reads clear also says its slot of recv may
+    // be refilled.  Each flag tile lies under exactly one workgroup's rows and
+    // columns when bits are consumed (checked on the host), so no other
+    // workgroup waits for the bits cleared here; the kernel's end makes the
+    // clears visible to whatever the stream runs next.
+    auto consume_ready = [&]() {
+    if constexpr (has_owner) {
+        if (!p.consume) return;
+        __syncthreads();
+        if (wave == 0)
+            with_items(true, [&](int items, auto item) {
+                for (int k = lane; k < items; k += 64) {
+                    uint32_t *word, bit;
+                    item(k, word, bit);
+                    fetch_and_relaxed(word, ~bit, sys);
+                }
+            });
     }
     };
 
@@ -1123,6 +1151,7 @@ __device__ __forceinline__ void gemm_rs_body(const GemmRsParams &p, uint8_t *sme
         for (int i = 0; i < TM; ++i) drain_block(i, -1, kAllRows);
         if (publishes) publish();
     }
+    consume_ready();
 }
 
 // ---- host side --------------------------------------------------------------------

@@ -86,8 +86,11 @@ enum {
     AREPI_TILE_PAIRED_ROWS = 0x200,
     /* ORed into any tile_cfg (AUTO included): the owner tiles clear each
      * ready_in bit they waited for, so ready_in is all zero again when the
-     * call ends and the next call can use it without a separate clear.  Needs
-     * the flag tiles to nest inside the compute tiles, as ready_out does. */
+     * call ends and the next call can use it without a separate clear.  A
+     * tile clears its bits only after every load of the data under them has
+     * returned (at the end of its epilogue), so a bit that reads clear also
+     * says its slot of recv may be refilled for the next call.  Needs the
+     * flag tiles to nest inside the compute tiles, as ready_out does. */
     AREPI_TILE_CONSUME_READY = 0x400,
     /* ORed into a contiguous tile_cfg (AUTO included) of arepi_gemm_rs_fused:
      * the owner segment's row blocks come first in the schedule instead of
@@ -389,21 +392,32 @@ int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, u
 /* Test-only: the emulated peers of `steps` consecutive consumer calls in one
  * launch, so that the producer is resident once for all of them.  Step s
  * lands the n_items items of orders[s % n_orders] (device int32
- * [n_orders][n_items][2]) exactly as arepi_emu_peer_producer does, after
- * waiting until *go >= s (device uint32, 0 before the launch; the consumer's
- * stream raises it with arepi_emu_signal(go, s, ...) once the consumer of
- * step s-1 has ended and no longer reads recv or ready_in).  That consumer
- * needs nothing from step s, so every wait ends; each is bounded by
- * spin_limit (encoding above), and on expiry the producer ORs
- * AREPI_STATUS_TIMEOUT into *status (status may be NULL) and stops.  Issue it
- * with `resident` and arepi_emu_producer_gate before the first consumer.
- * Errors: those of arepi_emu_peer_producer, plus go NULL, steps < 1 or
- * n_orders < 1. */
+ * [n_orders][n_items][2]) exactly as arepi_emu_peer_producer does, copying
+ * from src[p] + (s % n_orders) * src_step elements (src_step >= 0, a multiple
+ * of 8; 0: the same partials every step).  go: device uint32, 0 before the
+ * launch.  Pacing, one of two:
+ *   credit = 0 (signals): step s starts once *go >= s; the consumer's stream
+ *     raises it with arepi_emu_signal(go, s, ...) once the consumer of step
+ *     s-1 has ended and no longer reads recv or ready_in;
+ *   credit = 1: go is the producer's own count of landed (workgroup, step)
+ *     pairs; step s starts once every producer workgroup has landed step
+ *     s-1, and then each batch waits until the ready_in bits of its items are
+ *     clear, i.e. consumed.  The consumer must pass AREPI_TILE_CONSUME_READY,
+ *     whose owner tiles clear a bit only after the tile's data has been
+ *     read, so a slot is refilled as soon as it is free and no signal is
+ *     needed between consumer calls.
+ * The consumer of step s-1 needs nothing from step s, so every wait ends;
+ * each is bounded by spin_limit (encoding above), and on expiry the producer
+ * ORs AREPI_STATUS_TIMEOUT into *status (status may be NULL) and stops.
+ * Issue it with `resident` and arepi_emu_producer_gate before the first
+ * consumer.  Errors: those of arepi_emu_peer_producer, plus go NULL, credit
+ * not 0 or 1, steps < 1, n_orders < 1 or a bad src_step. */
 int arepi_emu_peer_producer_steps(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
                                   const int32_t *orders, int n_orders, int64_t n_items, int64_t M, int64_t N,
                                   int R, int owner, int flag_tile_m, int flag_tile_n, int scope, int workgroups,
-                                  int items_per_release, uint32_t *resident, const uint32_t *go, int steps,
-                                  uint32_t *status, int64_t spin_limit, arepi_stream_t stream);
+                                  int items_per_release, uint32_t *resident, uint32_t *go, int credit,
+                                  int steps, int64_t src_step, uint32_t *status, int64_t spin_limit,
+                                  arepi_stream_t stream);
 
 /* Test-only: a stream with a hardware queue of its own, for the emulated
  * producer.  The HIP runtime hands ordinary streams out of a small pool of

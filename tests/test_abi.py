@@ -208,8 +208,21 @@ def test_lamport_and_combine_validate_before_launch():
     assert L.arepi_emu_producer_gate(None, None, 0, None) == A.EINVAL
     assert "resident" in A.last_error()
     assert L.arepi_emu_peer_producer_steps(None, None, None, None, 1, 1, 256, 512, 2, 0, 128, 128, 0, 0, 1,
-                                           None, None, 2, None, 0, None) == A.EINVAL
+                                           None, None, 0, 2, 0, None, 0, None) == A.EINVAL
     assert "go" in A.last_error()
+    go = ctypes.c_void_p(16)  # never dereferenced: the calls below fail validation first
+    assert L.arepi_emu_peer_producer_steps(None, None, None, None, 1, 1, 256, 512, 2, 0, 128, 128, 0, 0, 1,
+                                           None, go, 2, 2, 0, None, 0, None) == A.EINVAL
+    assert "credit" in A.last_error()
+    assert L.arepi_emu_peer_producer_steps(None, None, None, None, 1, 1, 256, 512, 2, 0, 128, 128, 0, 0, 1,
+                                           None, go, 1, 2, 12, None, 0, None) == A.EINVAL
+    assert "src_step" in A.last_error()
+    assert L.arepi_emu_peer_producer_steps(None, None, None, None, 1, 1, 256, 512, 2, 0, 128, 128, 0, 0, 1,
+                                           None, go, 1, 0, 0, None, 0, None) == A.EINVAL
+    assert "steps" in A.last_error()
+    assert L.arepi_emu_peer_producer_steps(None, None, None, None, 1, 1, 256, 512, 2, 0, 128, 128, 0, 0, 1,
+                                           None, go, 1, 2, 0, None, 0, None) == A.EINVAL
+    assert "non-NULL" in A.last_error()
     assert L.arepi_emu_signal(None, 1, None) == A.EINVAL
 
 

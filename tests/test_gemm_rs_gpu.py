@@ -308,6 +308,79 @@ def test_one_producer_launch_feeds_consecutive_calls():
     assert int(go.item()) == 4
 
 
+def test_credit_producer_feeds_consecutive_calls_with_changing_partials():
+    """Credits instead of signals: the producer lands step s's partials into a
+    slot as soon as the call before has consumed its bit (the owner tiles
+    clear a bit only after reading the data under it), with no signal between
+    the calls.  The steps alternate between two different sets of partials,
+    so a slot refilled before the call before had read it would show up as
+    the other set's data in that call's output.  Every call equals the
+    pre-staged result of its set; ready_in and resident end zero."""
+    case = inputs.workload_gemm_rs(2)
+    M, N, K, R, owner = case["M"], case["N"], case["K"], case["R"], case["owner"]
+    seg = M // R
+    dev = device()
+    other = inputs.gemm_rs_case(M, N, K, R, owner=owner, seed=4242)
+    case_b = dict(case, recv=other["recv"])
+    pre = [run(case)["out"], run(case_b)["out"]]
+    assert not np.array_equal(pre[0], pre[1])
+    tiles = oracle.flag_tiles(M, N, R, 128, 128)
+    orders = torch.from_numpy(np.stack([inputs.producer_order(R, owner, tiles, 60 + i) for i in range(2)])).to(dev)
+    x, w = to_dev_bf16(case["x"]), to_dev_bf16(case["w"])
+    src = [None if p == owner else torch.stack([to_dev_bf16(case["recv"][p]), to_dev_bf16(other["recv"][p])])
+           for p in range(R)]
+    recv = [None if p == owner else torch.zeros((seg, N), dtype=torch.bfloat16, device=dev) for p in range(R)]
+    rin = torch.zeros((R, A.gemm_rs_flag_words(M, N, R)), dtype=torch.int32, device=dev)
+    rout = torch.zeros_like(rin)
+    send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    steps = 6
+    outs = [torch.empty((seg, N), dtype=torch.bfloat16, device=dev) for _ in range(steps)]
+    resident = torch.zeros(2, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    count = torch.zeros(1, dtype=torch.int32, device=dev)
+    side = A.emu_stream()
+    main = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print("credit producer, %d steps, two alternating sets" % steps, flush=True)
+    A.emu_peer_producer_steps(src, recv, rin, orders, R, owner, M, N, count, steps, workgroups=96,
+                              items_per_release=8, resident=resident, status=status, stream=side, credit=True)
+    A.emu_producer_gate(resident, status=status, stream=main)
+    for s in range(steps):
+        A.gemm_rs_fused(x, w, recv, rin, outs[s], R, owner, send=send, ready_out=rout,
+                        tile=A.TILE_CONSUME_READY, status=status, stream=main)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "a wait timed out"
+    for s in range(steps):
+        assert np.array_equal(from_dev_bf16(outs[s]), pre[s % 2]), "call %d" % s
+    assert not rin.any().item() and not resident.any().item()
+    assert int(count.item()) == 96 * steps
+
+
+def test_credit_producer_gives_up_on_unconsumed_bits():
+    """Every bit is still set (nothing consumed it): each batch's bounded wait
+    for its credit gives up, the producer reports the time-out and finishes
+    without touching recv."""
+    case = inputs.workload_gemm_rs(1)
+    M, N, R, owner = case["M"], case["N"], case["R"], case["owner"]
+    dev = device()
+    tiles = oracle.flag_tiles(M, N, R, 128, 128)
+    orders = torch.from_numpy(np.stack([inputs.producer_order(R, owner, tiles, 51)])).to(dev)
+    src = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
+    recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
+    full = flag_words_all_set(R, owner, tiles)
+    rin = to_dev_u32(full)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    count = torch.zeros(1, dtype=torch.int32, device=dev)
+    A.emu_peer_producer_steps(src, recv, rin, orders, R, owner, M, N, count, 2, status=status, spin_limit=2000,
+                              stream=A.emu_stream(), credit=True)
+    torch.cuda.synchronize()
+    assert int(status.item()) & A.STATUS_TIMEOUT
+    assert np.array_equal(from_dev_u32(rin), full)
+    for p in range(R):
+        if p != owner:
+            assert not recv[p].view(torch.int16).any().item()
+
+
 def test_multi_step_producer_gives_up_when_no_signal_comes():
     """Step 0 lands at once; step 1 waits for a signal the host never sends:
     the producer's bounded wait gives up, reports the time-out and the kernel
