@@ -99,7 +99,10 @@ __device__ void copy_item(const EmuParams &p, const int32_t *order, const int64_
 // the batch count paces the landing like a link of bounded rate.  Each batch:
 // copies, drain, barrier, one release, then its bits.
 // Its waves share the GPU with the GEMM it feeds, whose owner tiles spin on
-// these bits; a workgroup never waits, so once it is resident it finishes.
+// these bits.  A workgroup waits only between steps (for a signal, or for
+// the other workgroups and then for credits), and what it waits for comes
+// from a consumer of an earlier step, which needs nothing from it, so once it
+// is resident it finishes.
 // With `resident` given, every workgroup announces itself on arrival, so that
 // emu_gate_kernel can hold the consumer back until the whole grid has started.
 __global__ void __launch_bounds__(256) emu_producer_kernel(const EmuParams p) {
@@ -276,6 +279,8 @@ static int emu_launch(const char *who, const uint16_t *const *src, uint16_t *con
     p.spin_limit = spin_bound(spin_limit);
     const int64_t batches = (n_items + items_per_release - 1) / items_per_release;
     const int64_t groups = workgroups == 0 ? batches : std::min<int64_t>(workgroups, batches);
+    if (credit && (int64_t)steps * groups >= ((int64_t)1 << 32))
+        return bad("steps x workgroups must stay below 2^32 (the 32-bit landed-step count)");
     hipLaunchKernelGGL(emu_producer_kernel, dim3((unsigned)groups), dim3(256), 0,
                        reinterpret_cast<hipStream_t>(stream), p);
     return check_launch(who);

@@ -411,7 +411,8 @@ int arepi_emu_peer_producer(const uint16_t *const *src, uint16_t *const *recv, u
  * ORs AREPI_STATUS_TIMEOUT into *status (status may be NULL) and stops.
  * Issue it with `resident` and arepi_emu_producer_gate before the first
  * consumer.  Errors: those of arepi_emu_peer_producer, plus go NULL, credit
- * not 0 or 1, steps < 1, n_orders < 1 or a bad src_step. */
+ * not 0 or 1, steps < 1, n_orders < 1, a bad src_step, or (credit = 1)
+ * steps x launched workgroups reaching 2^32. */
 int arepi_emu_peer_producer_steps(const uint16_t *const *src, uint16_t *const *recv, uint32_t *ready_in,
                                   const int32_t *orders, int n_orders, int64_t n_items, int64_t M, int64_t N,
                                   int R, int owner, int flag_tile_m, int flag_tile_n, int scope, int workgroups,
@@ -437,9 +438,10 @@ int arepi_emu_signal(uint32_t *flag, uint32_t value, arepi_stream_t stream);
  * work must not be left unscheduled behind spinning consumers).  Launch it on
  * the consumer's stream after the producer (issued with the same `resident`)
  * and before the consumer: one wave waits until every producer workgroup has
- * started, then zeroes resident for the next step.  The producer never
- * waits, so once resident it finishes, whatever registers the consumer's
- * workgroups take.  Issue the producer first in host order: when the two
+ * started, then zeroes resident for the next step.  The producer waits only
+ * for consumers of earlier steps (or, within one call, not at all), which
+ * need nothing from it, so once resident it finishes, whatever registers the
+ * consumer's workgroups take.  Issue the producer first in host order: when the two
  * streams share one hardware queue, the queue then runs producer, gate and
  * consumer in turn.  The next producer on the same `resident` must be
  * ordered after this gate.  The wait is bounded by spin_limit (encoding as
