@@ -31,6 +31,7 @@ STATUS_TIMEOUT = 1
 TILE_PAIRED_ROWS = 0x200  # OR into an explicit tile: pair owner half-blocks with non-owner ones
 TILE_CONSUME_READY = 0x400  # OR into any tile: owner tiles clear the ready_in bits they waited for
 TILE_OWNER_FIRST = 0x800  # OR into a contiguous tile: the owner's row blocks first (partials already landed)
+TILE_OWNER_HALF = 0x1000  # OR into 256x256_w8_k64 (or AUTO): owner rows as 128x256 tiles after the rest
 LAMPORT_NOALLOC_BYTES = 32 * 1024 * 1024  # static staging of ar_rmsnorm_lamport_noalloc
 TILE_NAMES = {TILE_256x256: "256x256", TILE_128x256: "128x256", TILE_128x128: "128x128",
               TILE_64x128: "64x128", TILE_32x256: "32x256", TILE_256x256_S4: "256x256_s4",
@@ -174,7 +175,8 @@ def gemm_rs_supports(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publis
 
 def gemm_rs_schedule(M, N, K, R, owner, flag_tile_m=128, flag_tile_n=128, publish=False, tile=TILE_AUTO):
     """Work assignment of gemm_rs_fused: list of (row block, column block, a0, a_rows, b0, b_rows)
-    per workgroup in launch order (the rows it computes are [a0, a0+a_rows) and [b0, b0+b_rows))."""
+    per workgroup in launch order (the rows it computes are [a0, a0+a_rows) and [b0, b0+b_rows));
+    row block -1 marks the owner's half-height tiles (TILE_OWNER_HALF, or chosen by AUTO)."""
     n = _check(lib().arepi_gemm_rs_schedule(M, N, K, R, owner, flag_tile_m, flag_tile_n, int(publish), tile,
                                              None, 0), "gemm_rs_schedule")
     buf = (ctypes.c_int64 * (6 * n))()

@@ -41,6 +41,27 @@ extern "C" int arepi_gemm_rs_supports(int64_t M, int64_t N, int64_t K, int R, in
     if (rc) return rc;
     if ((tile_cfg & AREPI_TILE_OWNER_FIRST) && (tile_cfg & AREPI_TILE_PAIRED_ROWS))
         return fail(AREPI_EINVAL, "arepi_gemm_rs: AREPI_TILE_OWNER_FIRST needs the contiguous row layout");
+    if (tile_cfg & AREPI_TILE_OWNER_HALF) {
+        // owner rows as half-height tiles of the 8-wave 256x256 BK 64 tile
+        if (tile_cfg & (AREPI_TILE_PAIRED_ROWS | AREPI_TILE_OWNER_FIRST))
+            return fail(AREPI_EINVAL, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF needs the contiguous, owner-last layout");
+        const int base = tile_cfg & ~(AREPI_TILE_OWNER_HALF | AREPI_TILE_CONSUME_READY);
+        if (base != AREPI_TILE_AUTO && base != AREPI_TILE_256x256_W8_K64)
+            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF applies to AREPI_TILE_256x256_W8_K64");
+        const bool nest_h = publish || (tile_cfg & AREPI_TILE_CONSUME_READY);
+        if (base == AREPI_TILE_AUTO &&
+            arepi_gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m, flag_tile_n, nest_h) != AREPI_TILE_256x256_W8_K64)
+            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF with AUTO needs the 256x256_w8_k64 "
+                                            "tile to be the automatic choice");
+        if (R < 2 || (M / R) % 256)
+            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF needs R >= 2 and the segment "
+                                            "height M/R a multiple of 256");
+        if (!owner_half_fits(M, N, R, flag_tile_m, flag_tile_n, nest_h, AREPI_TILE_256x256_W8_K64))
+            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF: flag tiles " +
+                                                std::to_string(flag_tile_m) + "x" + std::to_string(flag_tile_n) +
+                                                " straddle the 128x256 owner tiles");
+        tile_cfg = (tile_cfg & AREPI_TILE_CONSUME_READY) | AREPI_TILE_256x256_W8_K64;
+    }
     tile_cfg &= ~AREPI_TILE_OWNER_FIRST;
     const bool consume = (tile_cfg & AREPI_TILE_CONSUME_READY) != 0;
     // consuming readiness bits needs the same nesting as publishing them
@@ -102,7 +123,8 @@ extern "C" int arepi_gemm_rs_fused(const uint16_t *x, const uint16_t *w, const u
     p.spin_limit = spin_bound(spin_limit);
     p.system_scope = scope == AREPI_SCOPE_SYSTEM;
     p.consume = c.consume ? 1 : 0;
-    rc = plan(p, c.t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous, c.owner_first);
+    rc = plan(p, c.t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous, c.owner_first,
+              c.owner_half);
     if (rc) return rc;
 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -124,22 +146,34 @@ extern "C" int64_t arepi_gemm_rs_schedule(int64_t M, int64_t N, int64_t K, int R
     const CfgChoice c = decode_cfg(M, N, K, R, flag_tile_m, flag_tile_n, publish != 0, tile_cfg);
     const TileCfg *t = c.t;
     GemmRsParams p{};
-    rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous, c.owner_first);
+    rc = plan(p, t, M, N, K, R, owner, flag_tile_m, flag_tile_n, c.nest, c.contiguous, c.owner_first,
+              c.owner_half);
     if (rc) return rc;
+    const int total = p.nWG + p.nextra;
     if (rows) {
-        if (capacity < (int64_t)p.nWG * 6)
+        if (capacity < (int64_t)total * 6)
             return fail(AREPI_EINVAL, "arepi_gemm_rs_schedule: capacity " + std::to_string(capacity) + " < 6 x " +
-                                          std::to_string(p.nWG) + " workgroups");
+                                          std::to_string(total) + " workgroups");
         const int CK = chunk_rows(t->BM);
-        for (int b = 0; b < p.nWG; ++b) {
+        for (int b = 0; b < total; ++b) {
             int rb, cb, alen, blen;
             int64_t a0, b0;
-            tile_of_block(p, b, rb, cb);
-            chunks_of_block(p, t->BM, CK, rb, a0, alen, b0, blen);
+            if (b < p.nWG) {
+                tile_of_block(p, b, rb, cb);
+                chunks_of_block(p, t->BM, CK, rb, a0, alen, b0, blen);
+            } else {
+                // owner half-height tile: row block -1, two chunks of BM/4 rows
+                int h;
+                owner_half_of_block(p, b, h, cb);
+                rb = -1;
+                a0 = (int64_t)owner * p.seg + (int64_t)h * (t->BM / 2);
+                alen = blen = t->BM / 4;
+                b0 = a0 + alen;
+            }
             int64_t *r = rows + (int64_t)b * 6;
             r[0] = rb, r[1] = cb, r[2] = a0, r[3] = alen, r[4] = b0, r[5] = blen;
         }
     }
     ok();
-    return p.nWG;
+    return total;
 }

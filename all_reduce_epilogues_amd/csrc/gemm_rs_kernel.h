@@ -23,6 +23,20 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     gemm_rs_kernel(const GemmRsParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<BM, BN, BK, S>()];
     constexpr int CK = BM >= 64 ? BM / 2 : BM;
+    // The 8-wave 256x256 BK 64 tile can run the owner segment as half-height
+    // tiles (BM/2 x BN with the same eight waves, WM/2 rows each) in the
+    // workgroups after the nWG others.
+    constexpr bool kHalfOwner = BM == 256 && BN == 256 && WM == 128 && WN == 64 && BK == 64 && S == 2;
+    if constexpr (kHalfOwner) {
+        if ((int)blockIdx.x >= p.nWG) {
+            int h, hcb;
+            owner_half_of_block(p, blockIdx.x, h, hcb);
+            const int64_t h0 = (int64_t)p.owner * p.seg + (int64_t)h * (BM / 2);
+            gemm_rs_body<BM / 2, BN, WM / 2, WN, BK, S, WPE, PEERS, kOwnerRowsAnywhere>(p, smem, -1, hcb, h0, BM / 4,
+                                                                                      h0 + BM / 4, BM / 4);
+            return;
+        }
+    }
     int rb, cb;
     tile_of_block(p, blockIdx.x, rb, cb);
     int64_t a0, b0;
@@ -58,13 +72,13 @@ template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, bool MIXED>
 void launch(const GemmRsParams &p, hipStream_t stream) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
     if (p.npeers <= 1)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1, MIXED>), dim3(p.nWG), dim3(NT), 0, stream,
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1, MIXED>), dim3(p.nWG + p.nextra), dim3(NT), 0, stream,
                            p);
     else if (p.npeers <= 3)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3, MIXED>), dim3(p.nWG), dim3(NT), 0, stream,
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3, MIXED>), dim3(p.nWG + p.nextra), dim3(NT), 0, stream,
                            p);
     else
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1, MIXED>), dim3(p.nWG), dim3(NT), 0,
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1, MIXED>), dim3(p.nWG + p.nextra), dim3(NT), 0,
                            stream, p);
 }
 

@@ -67,8 +67,9 @@ extern "C" int arepi_gemm_rs_ring_supports(int64_t M, int64_t N, int64_t K, int 
                                            int flag_tile_n, int publish, int tile_cfg) {
     if (tile_cfg & AREPI_TILE_PAIRED_ROWS)
         return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs_ring: AREPI_TILE_PAIRED_ROWS applies to the direct form only");
-    if (tile_cfg & AREPI_TILE_OWNER_FIRST)
-        return fail(AREPI_EINVAL, "arepi_gemm_rs_ring: AREPI_TILE_OWNER_FIRST is not an option of the ring order");
+    if (tile_cfg & (AREPI_TILE_OWNER_FIRST | AREPI_TILE_OWNER_HALF))
+        return fail(AREPI_EINVAL, "arepi_gemm_rs_ring: AREPI_TILE_OWNER_FIRST and AREPI_TILE_OWNER_HALF are not "
+                                  "options of the ring order");
     int rc = arepi_gemm_rs_supports(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish, tile_cfg);
     if (rc) return rc;
     if (R > 1 && (M / R) % kRingRowAlign)

@@ -332,12 +332,18 @@ def gemm_rs_prestaged(A, inputs, torch, iters, warmup, num, M=None, ring=False, 
     out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
     send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     tile = (A.gemm_rs_ring_pick_tile if ring else A.gemm_rs_pick_tile)(M, N, K, R, owner, publish=True)
+    name = A.TILE_NAMES[tile]
+    if not ring:
+        # the direct form runs the automatic choice, which may also split the
+        # owner rows into half-height tiles (row block -1 in the schedule)
+        if any(wg[0] == -1 for wg in A.gemm_rs_schedule(M, N, K, R, owner, publish=True)):
+            name += "+owner_half"
 
     def call():
         if ring:
             A.gemm_rs_ring(x, w, recv, rin, out, send, R, owner, ready_out=rout, tile=tile)
         else:
-            A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=tile)
+            A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, tile=A.TILE_AUTO)
 
     st = time_launches(torch, call, iters, warmup)
     flops = 2.0 * M * N * K
@@ -345,12 +351,12 @@ def gemm_rs_prestaged(A, inputs, torch, iters, warmup, num, M=None, ring=False, 
     t = st["ms_median"] * 1e-3
     # HBM-bound where the arithmetic intensity is below the ridge point
     hbm = flops / byts < (PEAK_BF16_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
-    traffic = measured_traffic(counters, A.TILE_NAMES[tile]) if counters else None
+    traffic = measured_traffic(counters, name) if counters else None
     rf = (roofline("hbm", byts, st, PEAK_HBM_GBS, "GB/s", traffic, "gemm_rs_ring_kernel" if ring else "gemm_rs_kernel")
           if hbm else
           roofline("mfma", flops, st, PEAK_BF16_TFLOPS, "TFLOP/s", traffic,
                    "gemm_rs_ring_kernel" if ring else "gemm_rs_kernel"))
-    res = dict(M=M, N=N, K=K, R=R, tile=A.TILE_NAMES[tile], **st, tflops=flops / t / 1e12,
+    res = dict(M=M, N=N, K=K, R=R, tile=name, **st, tflops=flops / t / 1e12,
                frac_mfma=flops / t / 1e12 / PEAK_BF16_TFLOPS, gbs=byts / t / 1e9,
                frac_hbm=byts / t / 1e9 / PEAK_HBM_GBS, roofline=rf)
     if not ring:

@@ -100,7 +100,17 @@ enum {
      * tiles' longer epilogue (R-1 partials read per tile) then overlaps the
      * later rounds instead of forming the last one.  Not with
      * AREPI_TILE_PAIRED_ROWS, not for the push ring or the fp8 form. */
-    AREPI_TILE_OWNER_FIRST = 0x800
+    AREPI_TILE_OWNER_FIRST = 0x800,
+    /* ORed into AREPI_TILE_256x256_W8_K64 (or AUTO where that tile is the
+     * automatic choice) of arepi_gemm_rs_fused, for grids of several rounds:
+     * the owner segment runs as 128x256 tiles (same eight waves, half the
+     * rows each) in workgroups after all the others, so each owner workgroup
+     * reads half the peers' bytes and the last round, which holds them, ends
+     * sooner.  Needs R >= 2, the segment height a multiple of 256, the
+     * contiguous owner-last layout, and (with ready_out or consumption) flag
+     * tiles nesting in 128x256 tiles.  AREPI_TILE_AUTO turns it on by itself
+     * where it applies and adds no round of workgroups. */
+    AREPI_TILE_OWNER_HALF = 0x1000
 };
 
 /* Message describing the last failed call on this thread ("" if none). */
@@ -152,7 +162,9 @@ int arepi_gemm_rs_supports(int64_t M, int64_t N, int64_t K, int R, int owner, in
 int64_t arepi_gemm_rs_flag_words(int64_t M, int64_t N, int R, int flag_tile_m, int flag_tile_n);
 
 /* Compute tile (AREPI_TILE_*) the automatic choice picks for a shape, or a
- * negative status. */
+ * negative status.  With AREPI_TILE_AUTO, arepi_gemm_rs_fused also applies
+ * AREPI_TILE_OWNER_HALF where it can and it adds no round of workgroups
+ * (at most 256 per round); passing the returned tile explicitly does not. */
 int arepi_gemm_rs_pick_tile(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
                             int flag_tile_n, int publish);
 
@@ -161,7 +173,8 @@ int arepi_gemm_rs_pick_tile(int64_t M, int64_t N, int64_t K, int R, int owner, i
  * rows is non-NULL (capacity >= 6*W int64 entries), workgroup b (in launch
  * order) gets rows[6b..6b+5] = {row block, column block, first row of chunk A,
  * rows of A, first row of chunk B, rows of B}; the workgroup computes the
- * output rows of both chunks over columns [column block * BN, + BN). */
+ * output rows of both chunks over columns [column block * BN, + BN).  Row
+ * block -1 marks an owner half-height tile (AREPI_TILE_OWNER_HALF). */
 int64_t arepi_gemm_rs_schedule(int64_t M, int64_t N, int64_t K, int R, int owner, int flag_tile_m,
                                int flag_tile_n, int publish, int tile_cfg, int64_t *rows,
                                int64_t capacity);

@@ -287,8 +287,11 @@ def test_owner_first_reorders_the_same_tiles(M, N, R, owner):
     puts them all in the first."""
     seg = M // R
     pub = A.gemm_rs_supports(M, N, 2048, R, owner, publish=True) == 0
-    base = np.asarray(A.gemm_rs_schedule(M, N, 2048, R, owner, publish=pub))
-    first = np.asarray(A.gemm_rs_schedule(M, N, 2048, R, owner, publish=pub, tile=A.TILE_OWNER_FIRST))
+    # the explicit tile of the automatic choice (AUTO alone may also split the
+    # owner rows into half-height tiles, which the owner-first order does not)
+    tile = A.gemm_rs_pick_tile(M, N, 2048, R, owner, publish=pub)
+    base = np.asarray(A.gemm_rs_schedule(M, N, 2048, R, owner, publish=pub, tile=tile))
+    first = np.asarray(A.gemm_rs_schedule(M, N, 2048, R, owner, publish=pub, tile=tile | A.TILE_OWNER_FIRST))
     assert sorted(map(tuple, base.tolist())) == sorted(map(tuple, first.tolist()))
 
     def owner_rows(s):
@@ -300,6 +303,69 @@ def test_owner_first_reorders_the_same_tiles(M, N, R, owner):
     assert idx[of].mean() < idx[~of].mean() and idx[ob].mean() > idx[~ob].mean()
     if len(base) > 256 and of.sum() <= 256:
         assert idx[of].max() < 256 and idx[ob].min() >= len(base) - 256 - 32
+
+
+@pytest.mark.parametrize("M,N,R,owner,tile", [(4096, 7168, 8, 0, 0), (4096, 7168, 8, 3, 11), (8192, 7168, 8, 5, 0),
+                                              (2048, 4096, 4, 1, 11), (512, 520, 2, 1, 11), (2048, 1032, 8, 7, 11)])
+def test_owner_half_tiles_cover_the_owner_segment_last(M, N, R, owner, tile):
+    """AREPI_TILE_OWNER_HALF: the owner segment's rows leave the 256x256
+    schedule and come after it as 128x256 workgroups (two 64-row chunks,
+    row block -1), one per half-block and column block; every row and column
+    block is covered exactly once, and no workgroup before them holds owner
+    rows."""
+    seg = M // R
+    sched = np.asarray(A.gemm_rs_schedule(M, N, 2048, R, owner, publish=True, tile=tile | A.TILE_OWNER_HALF))
+    ncb = -(-N // 256)
+    n_half = 2 * (seg // 256) * ncb
+    assert len(sched) == (M // 256) * ncb - (seg // 256) * ncb + n_half
+    head, tail = sched[:-n_half], sched[-n_half:]
+    assert not any(a0 // seg == owner or (blen and b0 // seg == owner) for _, _, a0, _, b0, blen in head)
+    assert (tail[:, 0] == -1).all() and (tail[:, 3] == 64).all() and (tail[:, 5] == 64).all()
+    assert (tail[:, 4] == tail[:, 2] + 64).all() and ((tail[:, 2] - owner * seg) % 128 == 0).all()
+    cover = np.zeros((M, ncb), np.int32)
+    for rb, cb, a0, alen, b0, blen in sched:
+        cover[a0:a0 + alen, cb] += 1
+        cover[b0:b0 + blen, cb] += 1
+    assert (cover == 1).all()
+
+
+def test_automatic_choice_uses_owner_half_tiles_where_no_round_is_added():
+    """AUTO splits the owner rows into half-height tiles when that keeps the
+    number of 256-workgroup rounds (tp=8 M = 2048, 4096, 8192), not for the
+    one-round tp=4 share (256 -> 320 workgroups), not where flag tiles of 256
+    rows must nest (consumed bits), and never when an explicit tile is given."""
+    def half(M, N, R, tile=A.TILE_AUTO, ftm=128, publish=True):
+        s = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, 128, publish=publish, tile=tile)
+        return any(w[0] == -1 for w in s), len(s)
+    assert half(4096, 4096, 4) == (False, 256)
+    assert half(2048, 7168, 8) == (True, 252)
+    assert half(4096, 7168, 8) == (True, 504)
+    assert half(8192, 7168, 8) == (True, 1008)
+    assert half(1024, 7168, 8)[0] is False  # 128-row segments
+    assert half(4096, 7168, 8, tile=A.TILE_256x256_W8_K64) == (False, 448)
+    assert half(4096, 7168, 8, tile=A.TILE_CONSUME_READY, ftm=256, publish=False)[0] is False
+    assert half(4096, 7168, 8, tile=A.TILE_CONSUME_READY, ftm=128, publish=False)[0] is True
+
+
+def test_owner_half_refusals():
+    t = A.TILE_OWNER_HALF
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t) == 0
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_256x256_W8_K64) == 0
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_256x256_W8_K64
+                              | A.TILE_PAIRED_ROWS) == A.EINVAL
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_OWNER_FIRST) == A.EINVAL
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_128x256) == A.EUNSUPPORTED
+    assert "256x256_W8_K64" in A.last_error()
+    assert A.gemm_rs_supports(1024, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_256x256_W8_K64) == \
+        A.EUNSUPPORTED  # 128-row segments
+    assert A.gemm_rs_supports(1024, 7168, 2048, 8, 0, publish=True, tile=t) == A.EUNSUPPORTED  # AUTO picks 128x256
+    assert A.gemm_rs_supports(4096, 7168, 2048, 1, 0, publish=True, tile=t | A.TILE_256x256_W8_K64) == \
+        A.EUNSUPPORTED
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, 256, 256, publish=True, tile=t | A.TILE_256x256_W8_K64) == \
+        A.EUNSUPPORTED  # 256-row flag tiles straddle the 128-row owner tiles
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, 256, 256, publish=False, tile=t | A.TILE_256x256_W8_K64) == 0
+    assert A.gemm_rs_ring_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t) == A.EINVAL
+    assert A.gemm_rs_fp8_supports(512, 512, 256, 2, 0, tile=t) != 0
 
 
 def test_owner_first_refuses_paired_rows_ring_and_fp8():

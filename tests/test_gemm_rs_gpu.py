@@ -82,8 +82,9 @@ def tiles_to_try(case, ftm, ftn):
 
 
 def tile_name(t):
-    base = t & ~A.TILE_PAIRED_ROWS
-    return A.TILE_NAMES.get(base, "auto") + ("/paired" if t & A.TILE_PAIRED_ROWS else "")
+    base = t & 0xff
+    return A.TILE_NAMES.get(base, "auto") + ("/paired" if t & A.TILE_PAIRED_ROWS else "") + \
+        ("/owner-half" if t & A.TILE_OWNER_HALF else "")
 
 
 @pytest.mark.parametrize("owner", [0, 1])
@@ -141,6 +142,24 @@ def test_owner_first_order_every_tile(M, N, K, R, owner, ftm, ftn):
         print("owner-first %s tile=%s publish=%s" % ((M, N, K, R, owner), tile_name(base), pub), flush=True)
         res = run(case, tile=tile, publish=pub, ftm=ftm, ftn=ftn)
         check_against_oracle(case, res, ftm, ftn, what="owner-first/%s" % tile_name(base), ref=ref)
+
+
+@pytest.mark.parametrize("M,N,K,R,owner", [
+    (512, 520, 136, 2, 1),      # N tail, K tail, one 256-row segment
+    (2048, 1032, 200, 8, 7),    # last segment owns, N tail
+    (4096, 7168, 256, 8, 3),    # two rounds of workgroups at the model width
+])
+def test_owner_half_tiles(M, N, K, R, owner):
+    """AREPI_TILE_OWNER_HALF: the owner rows as 128x256 workgroups after the
+    256x256 ones, the same arithmetic per element."""
+    case = inputs.gemm_rs_case(M, N, K, R, owner=owner, seed=17 + M + N + K)
+    ref = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
+    for tile in (A.TILE_256x256_W8_K64 | A.TILE_OWNER_HALF, A.TILE_AUTO | A.TILE_OWNER_HALF):
+        if A.gemm_rs_supports(M, N, K, R, owner, publish=True, tile=tile) != 0:
+            continue  # AUTO picks another tile for this shape
+        print("owner-half %s tile=%#x" % ((M, N, K, R, owner), tile), flush=True)
+        res = run(case, tile=tile, publish=True)
+        check_against_oracle(case, res, what="owner-half %#x" % tile, ref=ref)
 
 
 def test_golden_all_ones_two_ranks_on_gpu():
@@ -418,7 +437,8 @@ def test_gate_times_out_when_no_producer_announces():
 
 @pytest.mark.parametrize("M,owner,tile", [(256, 0, A.TILE_AUTO), (1024, 0, A.TILE_AUTO), (1024, 7, A.TILE_AUTO),
                                           (4096, 0, A.TILE_AUTO), (8192, 0, A.TILE_AUTO),
-                                          (4096, 5, A.TILE_OWNER_FIRST), (8192, 0, A.TILE_OWNER_FIRST)])
+                                          (4096, 5, A.TILE_OWNER_FIRST), (8192, 0, A.TILE_OWNER_FIRST),
+                                          (4096, 2, A.TILE_OWNER_HALF), (8192, 7, A.TILE_OWNER_HALF)])
 def test_tp8_workload_sweep(M, owner, tile):
     case = inputs.workload_gemm_rs(3, M=M, owner=owner)
     R = 8
@@ -446,6 +466,7 @@ def test_timeout_reports_status_and_finishes():
 
 @pytest.mark.parametrize("M,N,K,R,owner,ftm,ftn,tile", [
     (2048, 2048, 512, 4, 0, 128, 128, A.TILE_AUTO),
+    (2048, 1032, 200, 8, 7, 128, 128, A.TILE_256x256_W8_K64 | A.TILE_OWNER_HALF),
     (1024, 7168, 256, 8, 3, 128, 128, A.TILE_256x256_W8 | A.TILE_PAIRED_ROWS),
     (640, 1032, 200, 5, 3, 64, 128, A.TILE_AUTO),
     (384, 264, 72, 3, 2, 32, 8, A.TILE_128x128_S4),
