@@ -207,11 +207,15 @@ __host__ __device__ __forceinline__ void tile_of_block(const GemmRsParams &p, in
 
 // Workgroup b >= nWG of the owner half-height tiles: half-block h of the
 // owner segment (BM/2 rows from owner*seg + h*BM/2), column block cb.  The
-// half-blocks of one column block are consecutive.
+// half-blocks of one column block are consecutive entries, and the entries
+// are remapped as tile_of_block remaps a round (when their count is a
+// multiple of 8), so that consecutive entries land on one XCD and share its
+// L2's copy of the W column block.
 __host__ __device__ __forceinline__ void owner_half_of_block(const GemmRsParams &p, int b, int &h, int &cb) {
-    const int i = b - p.nWG, nh = p.nextra / p.nCB;
-    h = i % nh;
-    cb = i / nh;
+    const int j = b - p.nWG, nh = p.nextra / p.nCB;
+    const int s = p.nextra % kXcds == 0 ? (j % kXcds) * (p.nextra / kXcds) + j / kXcds : j;
+    h = s % nh;
+    cb = s / nh;
 }
 
 // LDS bytes of one workgroup: S stages of [X tile | W tile].
