@@ -42,25 +42,27 @@ extern "C" int arepi_gemm_rs_supports(int64_t M, int64_t N, int64_t K, int R, in
     if ((tile_cfg & AREPI_TILE_OWNER_FIRST) && (tile_cfg & AREPI_TILE_PAIRED_ROWS))
         return fail(AREPI_EINVAL, "arepi_gemm_rs: AREPI_TILE_OWNER_FIRST needs the contiguous row layout");
     if (tile_cfg & AREPI_TILE_OWNER_HALF) {
-        // owner rows as half-height tiles of the 8-wave 256x256 BK 64 tile
+        // owner rows as half-height tiles (256x256_w8_k64 and 128x256 only)
         if (tile_cfg & (AREPI_TILE_PAIRED_ROWS | AREPI_TILE_OWNER_FIRST))
             return fail(AREPI_EINVAL, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF needs the contiguous, owner-last layout");
-        const int base = tile_cfg & ~(AREPI_TILE_OWNER_HALF | AREPI_TILE_CONSUME_READY);
-        if (base != AREPI_TILE_AUTO && base != AREPI_TILE_256x256_W8_K64)
-            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF applies to AREPI_TILE_256x256_W8_K64");
-        const bool nest_h = publish || (tile_cfg & AREPI_TILE_CONSUME_READY);
-        if (base == AREPI_TILE_AUTO &&
-            arepi_gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m, flag_tile_n, nest_h) != AREPI_TILE_256x256_W8_K64)
-            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF with AUTO needs the 256x256_w8_k64 "
-                                            "tile to be the automatic choice");
-        if (R < 2 || (M / R) % 256)
+        const bool consume_h = (tile_cfg & AREPI_TILE_CONSUME_READY) != 0;
+        int base = tile_cfg & ~(AREPI_TILE_OWNER_HALF | AREPI_TILE_CONSUME_READY);
+        if (base == AREPI_TILE_AUTO) {
+            base = arepi_gemm_rs_pick_tile(M, N, K, R, owner, flag_tile_m, flag_tile_n, publish || consume_h);
+            if (base < 0) return base;
+        }
+        if (!has_owner_half(base))
+            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF applies to AREPI_TILE_256x256_W8_K64 "
+                                            "and AREPI_TILE_128x256 (explicit, or as the automatic choice)");
+        const int bm = find_tile(base)->BM;
+        if (R < 2 || (M / R) % bm)
             return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF needs R >= 2 and the segment "
-                                            "height M/R a multiple of 256");
-        if (!owner_half_fits(M, N, R, flag_tile_m, flag_tile_n, nest_h, AREPI_TILE_256x256_W8_K64))
-            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF: flag tiles " +
+                                            "height M/R a multiple of " + std::to_string(bm));
+        if (!owner_half_fits(M, N, R, flag_tile_m, flag_tile_n, consume_h, base))
+            return fail(AREPI_EUNSUPPORTED, "arepi_gemm_rs: AREPI_TILE_OWNER_HALF: consumed flag tiles " +
                                                 std::to_string(flag_tile_m) + "x" + std::to_string(flag_tile_n) +
-                                                " straddle the 128x256 owner tiles");
-        tile_cfg = (tile_cfg & AREPI_TILE_CONSUME_READY) | AREPI_TILE_256x256_W8_K64;
+                                                " straddle the " + std::to_string(bm / 2) + "-row owner tiles");
+        tile_cfg = (tile_cfg & AREPI_TILE_CONSUME_READY) | base;
     }
     tile_cfg &= ~AREPI_TILE_OWNER_FIRST;
     const bool consume = (tile_cfg & AREPI_TILE_CONSUME_READY) != 0;

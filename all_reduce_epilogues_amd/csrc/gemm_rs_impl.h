@@ -1332,12 +1332,17 @@ int plan(GemmRsParams &p, const TileCfg *t, int64_t M, int64_t N, int64_t K, int
     return AREPI_OK;
 }
 
-// Whether AREPI_TILE_OWNER_HALF can apply: the 8-wave 256x256 BK 64 tile,
-// whole 256-row owner blocks, and flag tiles nesting in the 128x256 owner
-// tiles when bits are published or consumed.
-bool owner_half_fits(int64_t M, int64_t N, int R, int ftm, int ftn, bool nest, int id) {
-    return id == AREPI_TILE_256x256_W8_K64 && R >= 2 && (M / R) % 256 == 0 &&
-           (!nest || flags_nest(M, N, R, ftm, ftn, 128, 256));
+// Tiles with an owner half-height form (AREPI_TILE_OWNER_HALF): the 8-wave
+// 256x256 BK 64 tile and the 4-wave 128x256 tile.
+bool has_owner_half(int id) { return id == AREPI_TILE_256x256_W8_K64 || id == AREPI_TILE_128x256; }
+
+// Whether AREPI_TILE_OWNER_HALF can apply to tile id: whole owner row blocks,
+// and, when bits are consumed, flag tiles nesting in the half-height owner
+// tiles (each must lie under one workgroup; owner tiles publish nothing).
+bool owner_half_fits(int64_t M, int64_t N, int R, int ftm, int ftn, bool consume, int id) {
+    if (!has_owner_half(id) || R < 2) return false;
+    const TileCfg *t = find_tile(id);
+    return (M / R) % t->BM == 0 && (!consume || flags_nest(M, N, R, ftm, ftn, t->BM / 2, t->BN));
 }
 
 // Tile id, row layout and options of a validated tile_cfg.
@@ -1362,9 +1367,12 @@ CfgChoice decode_cfg(int64_t M, int64_t N, int64_t K, int R, int ftm, int ftn, b
     // runs the owner rows as half-height tiles where that adds no round of
     // workgroups: tp=8 M = 2048, 4096, 8192 measured 13%, 7% and 6% faster;
     // the one-round tp=4 share would need a second round.
-    if (id == AREPI_TILE_AUTO && !whole_segments && c.contiguous && !c.owner_first && owner_half_fits(M, N, R, ftm, ftn, c.nest, c.id)) {
-        const int64_t ncb = cdiv(N, 256), plain = cdiv(M, 256) * ncb, half = plain + (M / R / 256) * ncb;
-        if (cdiv(half, 256) <= cdiv(plain, 256)) c.owner_half = true;
+    if (id == AREPI_TILE_AUTO && !whole_segments && c.contiguous && !c.owner_first &&
+        owner_half_fits(M, N, R, ftm, ftn, c.consume, c.id)) {
+        const int64_t ncb = cdiv(N, c.t->BN), plain = cdiv(M, c.t->BM) * ncb;
+        const int64_t half = plain + (M / R / c.t->BM) * ncb;
+        const int64_t round = 256 * (int64_t)c.t->slots;
+        if (cdiv(half, round) <= cdiv(plain, round)) c.owner_half = true;
     }
     return c;
 }

@@ -23,10 +23,11 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
     gemm_rs_kernel(const GemmRsParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[lds_bytes<BM, BN, BK, S>()];
     constexpr int CK = BM >= 64 ? BM / 2 : BM;
-    // The 8-wave 256x256 BK 64 tile can run the owner segment as half-height
-    // tiles (BM/2 x BN with the same eight waves, WM/2 rows each) in the
-    // workgroups after the nWG others.
-    constexpr bool kHalfOwner = BM == 256 && BN == 256 && WM == 128 && WN == 64 && BK == 64 && S == 2;
+    // The 8-wave 256x256 BK 64 tile and the 4-wave 128x256 tile can run the
+    // owner segment as half-height tiles (BM/2 x BN with the same waves, WM/2
+    // rows each) in the workgroups after the nWG others.
+    constexpr bool kHalfOwner = BN == 256 && BK == 64 && S == 2 &&
+                                ((BM == 256 && WM == 128 && WN == 64) || (BM == 128 && WM == 64 && WN == 128));
     if constexpr (kHalfOwner) {
         if ((int)blockIdx.x >= p.nWG) {
             int h, hcb;

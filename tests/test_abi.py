@@ -267,15 +267,22 @@ def test_owner_half_blocks_pair_on_the_model_shapes(M, N, R):
 @pytest.mark.parametrize("M,N,R", [(4096, 4096, 4), (1024, 7168, 8), (200, 520, 2)])
 def test_consume_option_plans_like_publication(M, N, R):
     """AREPI_TILE_CONSUME_READY picks and lays out tiles as publication does
-    (both need every flag tile under one workgroup)."""
+    (both need every flag tile under one workgroup).  The automatic owner
+    half-height tiles are the one difference: consumed bits also need each
+    flag tile under one owner tile, published ones do not."""
     for ftm, ftn in ((128, 128), (32, 64)):
         auto = A.gemm_rs_pick_tile(M, N, 2048, R, 0, ftm, ftn, publish=True)
         if auto < 0:
             assert A.gemm_rs_supports(M, N, 2048, R, 0, ftm, ftn, tile=A.TILE_CONSUME_READY) < 0
             continue
-        ref = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=True)
-        got = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=False, tile=A.TILE_CONSUME_READY)
+        ref = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=True, tile=auto)
+        got = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=False, tile=auto | A.TILE_CONSUME_READY)
         assert np.array_equal(ref, got)
+        half_pub = any(w[0] == -1 for w in A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=True))
+        half_con = any(w[0] == -1 for w in A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, ftn, publish=False,
+                                                                tile=A.TILE_CONSUME_READY))
+        owner_rows = A.TILE_DIMS[auto][0] // 2
+        assert half_con == (half_pub and owner_rows % ftm == 0)
 
 
 @pytest.mark.parametrize("M,N,R,owner", [(4096, 7168, 8, 3), (8192, 7168, 8, 0), (1024, 7168, 8, 5),
@@ -306,22 +313,24 @@ def test_owner_first_reorders_the_same_tiles(M, N, R, owner):
 
 
 @pytest.mark.parametrize("M,N,R,owner,tile", [(4096, 7168, 8, 0, 0), (4096, 7168, 8, 3, 11), (8192, 7168, 8, 5, 0),
-                                              (2048, 4096, 4, 1, 11), (512, 520, 2, 1, 11), (2048, 1032, 8, 7, 11)])
+                                              (2048, 4096, 4, 1, 11), (512, 520, 2, 1, 11), (2048, 1032, 8, 7, 11),
+                                              (1024, 7168, 8, 3, 0), (1024, 1032, 8, 0, 2), (384, 520, 3, 2, 2)])
 def test_owner_half_tiles_cover_the_owner_segment_last(M, N, R, owner, tile):
-    """AREPI_TILE_OWNER_HALF: the owner segment's rows leave the 256x256
-    schedule and come after it as 128x256 workgroups (two 64-row chunks,
+    """AREPI_TILE_OWNER_HALF: the owner segment's rows leave the BM x 256
+    schedule and come after it as BM/2 x 256 workgroups (two BM/4-row chunks,
     row block -1), one per half-block and column block; every row and column
     block is covered exactly once, and no workgroup before them holds owner
     rows."""
     seg = M // R
+    BM = A.TILE_DIMS[tile or A.gemm_rs_pick_tile(M, N, 2048, R, owner, publish=True)][0]
     sched = np.asarray(A.gemm_rs_schedule(M, N, 2048, R, owner, publish=True, tile=tile | A.TILE_OWNER_HALF))
     ncb = -(-N // 256)
-    n_half = 2 * (seg // 256) * ncb
-    assert len(sched) == (M // 256) * ncb - (seg // 256) * ncb + n_half
+    n_half = 2 * (seg // BM) * ncb
+    assert len(sched) == (M // BM) * ncb - (seg // BM) * ncb + n_half
     head, tail = sched[:-n_half], sched[-n_half:]
     assert not any(a0 // seg == owner or (blen and b0 // seg == owner) for _, _, a0, _, b0, blen in head)
-    assert (tail[:, 0] == -1).all() and (tail[:, 3] == 64).all() and (tail[:, 5] == 64).all()
-    assert (tail[:, 4] == tail[:, 2] + 64).all() and ((tail[:, 2] - owner * seg) % 128 == 0).all()
+    assert (tail[:, 0] == -1).all() and (tail[:, 3] == BM // 4).all() and (tail[:, 5] == BM // 4).all()
+    assert (tail[:, 4] == tail[:, 2] + BM // 4).all() and ((tail[:, 2] - owner * seg) % (BM // 2) == 0).all()
     cover = np.zeros((M, ncb), np.int32)
     for rb, cb, a0, alen, b0, blen in sched:
         cover[a0:a0 + alen, cb] += 1
@@ -331,9 +340,10 @@ def test_owner_half_tiles_cover_the_owner_segment_last(M, N, R, owner, tile):
 
 def test_automatic_choice_uses_owner_half_tiles_where_no_round_is_added():
     """AUTO splits the owner rows into half-height tiles when that keeps the
-    number of 256-workgroup rounds (tp=8 M = 2048, 4096, 8192), not for the
-    one-round tp=4 share (256 -> 320 workgroups), not where flag tiles of 256
-    rows must nest (consumed bits), and never when an explicit tile is given."""
+    number of 256-workgroup rounds (tp=8 M = 1024, 2048, 4096, 8192), not for
+    the one-round tp=4 share (256 -> 320 workgroups), not where consumed flag
+    tiles would straddle two owner tiles, and never when an explicit tile is
+    given."""
     def half(M, N, R, tile=A.TILE_AUTO, ftm=128, publish=True):
         s = A.gemm_rs_schedule(M, N, 2048, R, 0, ftm, 128, publish=publish, tile=tile)
         return any(w[0] == -1 for w in s), len(s)
@@ -341,10 +351,11 @@ def test_automatic_choice_uses_owner_half_tiles_where_no_round_is_added():
     assert half(2048, 7168, 8) == (True, 252)
     assert half(4096, 7168, 8) == (True, 504)
     assert half(8192, 7168, 8) == (True, 1008)
-    assert half(1024, 7168, 8)[0] is False  # 128-row segments
+    assert half(1024, 7168, 8) == (True, 252)  # 128x256 tiles, owner rows as 64x256: still one round
     assert half(4096, 7168, 8, tile=A.TILE_256x256_W8_K64) == (False, 448)
     assert half(4096, 7168, 8, tile=A.TILE_CONSUME_READY, ftm=256, publish=False)[0] is False
     assert half(4096, 7168, 8, tile=A.TILE_CONSUME_READY, ftm=128, publish=False)[0] is True
+    assert half(1024, 7168, 8, tile=A.TILE_CONSUME_READY, ftm=128, publish=False)[0] is False  # 64-row owner tiles
 
 
 def test_owner_half_refusals():
@@ -354,16 +365,18 @@ def test_owner_half_refusals():
     assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_256x256_W8_K64
                               | A.TILE_PAIRED_ROWS) == A.EINVAL
     assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_OWNER_FIRST) == A.EINVAL
-    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_128x256) == A.EUNSUPPORTED
-    assert "256x256_W8_K64" in A.last_error()
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_128x256) == 0
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_128x128) == A.EUNSUPPORTED
+    assert "AREPI_TILE_128x256" in A.last_error()
     assert A.gemm_rs_supports(1024, 7168, 2048, 8, 0, publish=True, tile=t | A.TILE_256x256_W8_K64) == \
         A.EUNSUPPORTED  # 128-row segments
-    assert A.gemm_rs_supports(1024, 7168, 2048, 8, 0, publish=True, tile=t) == A.EUNSUPPORTED  # AUTO picks 128x256
+    assert A.gemm_rs_supports(1024, 7168, 2048, 8, 0, publish=True, tile=t) == 0  # AUTO picks 128x256
     assert A.gemm_rs_supports(4096, 7168, 2048, 1, 0, publish=True, tile=t | A.TILE_256x256_W8_K64) == \
         A.EUNSUPPORTED
-    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, 256, 256, publish=True, tile=t | A.TILE_256x256_W8_K64) == \
-        A.EUNSUPPORTED  # 256-row flag tiles straddle the 128-row owner tiles
-    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, 256, 256, publish=False, tile=t | A.TILE_256x256_W8_K64) == 0
+    # 256-row flag tiles straddle the 128-row owner tiles: fine for waiting, not for consuming
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, 256, 256, publish=True, tile=t | A.TILE_256x256_W8_K64) == 0
+    assert A.gemm_rs_supports(4096, 7168, 2048, 8, 0, 256, 256, publish=True,
+                              tile=t | A.TILE_256x256_W8_K64 | A.TILE_CONSUME_READY) == A.EUNSUPPORTED
     assert A.gemm_rs_ring_supports(4096, 7168, 2048, 8, 0, publish=True, tile=t) == A.EINVAL
     assert A.gemm_rs_fp8_supports(512, 512, 256, 2, 0, tile=t) != 0
 

@@ -148,16 +148,19 @@ def test_owner_first_order_every_tile(M, N, K, R, owner, ftm, ftn):
     (512, 520, 136, 2, 1),      # N tail, K tail, one 256-row segment
     (2048, 1032, 200, 8, 7),    # last segment owns, N tail
     (4096, 7168, 256, 8, 3),    # two rounds of workgroups at the model width
+    (384, 520, 72, 3, 2),       # R=3, 128-row segments: the 128x256 tile's 64-row owner tiles
+    (1024, 7168, 256, 8, 5),    # the tp=8 M=1024 shape
 ])
 def test_owner_half_tiles(M, N, K, R, owner):
-    """AREPI_TILE_OWNER_HALF: the owner rows as 128x256 workgroups after the
-    256x256 ones, the same arithmetic per element."""
+    """AREPI_TILE_OWNER_HALF: the owner rows as half-height workgroups after
+    the others, the same arithmetic per element."""
     case = inputs.gemm_rs_case(M, N, K, R, owner=owner, seed=17 + M + N + K)
     ref = oracle.gemm_rs(case["x"], case["w"], case["recv"], R, owner)
-    for tile in (A.TILE_256x256_W8_K64 | A.TILE_OWNER_HALF, A.TILE_AUTO | A.TILE_OWNER_HALF):
+    for tile in (A.TILE_256x256_W8_K64 | A.TILE_OWNER_HALF, A.TILE_128x256 | A.TILE_OWNER_HALF,
+                 A.TILE_AUTO | A.TILE_OWNER_HALF):
         if A.gemm_rs_supports(M, N, K, R, owner, publish=True, tile=tile) != 0:
             continue  # AUTO picks another tile for this shape
-        print("owner-half %s tile=%#x" % ((M, N, K, R, owner), tile), flush=True)
+        print("owner-half %s tile=%s" % ((M, N, K, R, owner), tile_name(tile)), flush=True)
         res = run(case, tile=tile, publish=True)
         check_against_oracle(case, res, what="owner-half %#x" % tile, ref=ref)
 
