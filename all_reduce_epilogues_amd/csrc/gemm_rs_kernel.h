@@ -37,6 +37,8 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
                                                                                       h0 + BM / 4, BM / 4);
             return;
         }
+    } else {
+        if ((int)blockIdx.x >= p.nWG) return;  // (the host never launches extra workgroups for this tile)
     }
     int rb, cb;
     tile_of_block(p, blockIdx.x, rb, cb);
@@ -72,15 +74,14 @@ __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 template <int BM, int BN, int WM, int WN, int BK, int S, int WPE, bool MIXED>
 void launch(const GemmRsParams &p, hipStream_t stream) {
     constexpr int NT = (BM / WM) * (BN / WN) * 64;
+    const dim3 grid(p.nWG + p.nextra);  // the owner half-height workgroups come after the others
     if (p.npeers <= 1)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1, MIXED>), dim3(p.nWG + p.nextra), dim3(NT), 0, stream,
-                           p);
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 1, MIXED>), grid, dim3(NT), 0, stream, p);
     else if (p.npeers <= 3)
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3, MIXED>), dim3(p.nWG + p.nextra), dim3(NT), 0, stream,
-                           p);
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, 3, MIXED>), grid, dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1, MIXED>), dim3(p.nWG + p.nextra), dim3(NT), 0,
-                           stream, p);
+        hipLaunchKernelGGL((gemm_rs_kernel<BM, BN, WM, WN, BK, S, WPE, kMaxR - 1, MIXED>), grid, dim3(NT), 0, stream,
+                           p);
 }
 
 // Launches tile `cfg`; false if there is no kernel for it.
