@@ -248,6 +248,43 @@ def test_tp4_workload_prestaged_and_concurrent_producer():
         assert np.array_equal(from_dev_u32(rin), flag_words_all_set(R, owner, tiles))
 
 
+@pytest.mark.parametrize("M", [1024, 4096])
+def test_owner_half_tiles_with_a_concurrent_producer(M):
+    """tp=8 shapes where the automatic choice runs the owner rows as
+    half-height tiles: the peers' partials land tile by tile in a shuffled
+    order while the GEMM runs, so the half-height owner workgroups really
+    wait; the result equals the pre-staged one bit for bit."""
+    case = inputs.workload_gemm_rs(3, M=M, owner=3)
+    N, R, owner = case["N"], case["R"], case["owner"]
+    seg = M // R
+    assert any(wg[0] == -1 for wg in A.gemm_rs_schedule(M, N, case["K"], R, owner, publish=True))
+    pre = run(case)
+    dev = device()
+    tiles = oracle.flag_tiles(M, N, R, 128, 128)
+    order = torch.from_numpy(inputs.producer_order(R, owner, tiles, 70 + M)).to(dev)
+    src = [None if p == owner else to_dev_bf16(case["recv"][p]) for p in range(R)]
+    recv = [None if p == owner else torch.zeros_like(src[p]) for p in range(R)]
+    rin = torch.zeros((R, A.gemm_rs_flag_words(M, N, R)), dtype=torch.int32, device=dev)
+    out = torch.empty((seg, N), dtype=torch.bfloat16, device=dev)
+    send = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    rout = torch.zeros_like(rin)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    resident = torch.zeros(2, dtype=torch.int32, device=dev)
+    x, w = to_dev_bf16(case["x"]), to_dev_bf16(case["w"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    print("owner-half tp=8 M=%d, concurrent producer" % M, flush=True)
+    A.emu_peer_producer(src, recv, rin, order, R, owner, M, N, workgroups=48, items_per_release=4,
+                        resident=resident, stream=side)
+    A.emu_producer_gate(resident, status=status, stream=main)
+    A.gemm_rs_fused(x, w, recv, rin, out, R, owner, send=send, ready_out=rout, status=status, stream=main)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "a readiness wait timed out"
+    assert np.array_equal(from_dev_bf16(out), pre["out"])
+    assert np.array_equal(from_dev_u32(rout), oracle.ready_out(M, N, R, owner, 128, 128))
+
+
 def test_gate_lets_the_producer_finish_beside_a_register_full_gemm():
     """The 4-wave 256x256 tile at R = 4 allocates all 512 registers per SIMD
     lane, so no producer wave fits beside it on a compute unit.  The gate,
