@@ -26,14 +26,18 @@
 //    scheduling groups.
 //  * Rows: a row block is two half-blocks (chunks) of BM/2 rows, interleaved
 //    between the wave rows.  Optionally (AREPI_TILE_PAIRED_ROWS) an owner
-//    half-block is paired with a non-owner one.
+//    half-block is paired with a non-owner one; or (AREPI_TILE_OWNER_HALF)
+//    the owner rows run as half-height tiles of the same waves after all the
+//    other workgroups.
 //  * Epilogue, chosen per workgroup at entry (no-owner / owner-chunk-A /
 //    owner-rows-anywhere bodies): accumulators go through LDS one 32-row slab
 //    at a time and come back row-contiguous; owner rows wait for their peers'
 //    flag-tile bits (one lane per (peer, tile), relaxed polls, one acquire),
 //    add the peers' packs (fetched several units ahead with row-coalesced
 //    loads, ascending rank order, fp32) and store to `out`; other rows are
-//    stored to `send`.  Stores are buffer stores whose out-of-range offsets
+//    stored to `send`.  With consumption, an owner tile clears the bits it
+//    waited for at its end, once every load of the data under them has
+//    returned.  Stores are buffer stores whose out-of-range offsets
 //    drop lanes, so the code has no data-dependent branches around memory
 //    operations.  No per-tile drain on `out` (the kernel end is its release);
 //    a drain + balanced barrier + one release precede the ready_out bits.
